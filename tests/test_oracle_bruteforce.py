@@ -222,9 +222,9 @@ def test_four_over_six_1x16_matches_exact_model(seed, err_mode, bound, row):
 
 @pytest.mark.parametrize("err_mode", ["mae", "mse"])
 def test_four_over_six_16x16_matches_exact_model(err_mode):
-    x = _inputs(31, 16, 32)
+    x = _inputs(31, 32, 64)
     A = oracle.amax(x)
-    codes, sb = _model_4over6(x, [exact(A)] * 16, err_mode, 256, "16x16")
+    codes, sb = _model_4over6(x, [exact(A)] * 32, err_mode, 256, "16x16")
     packed, scales = oracle.quantize_4over6(x, A, err_mode=err_mode, bound=256, block="16x16")
     assert np.array_equal(scales, sb)
     assert np.array_equal(unpack_codes(packed), codes)
@@ -257,3 +257,22 @@ def test_2d_matches_exact_model(stochastic):
     assert np.array_equal(s, sb)
     assert np.array_equal(unpack_codes(r), codes)
     assert np.array_equal(unpack_codes(c), codes.T)
+
+
+def test_tile_error_tree_order():
+    # Four-over-six pull request, CuTe DSL kernel Design: the 16 row errors of
+    # a 16x16 tile are combined by one fixed width-16 tree.  Mixed magnitudes
+    # make every association give a different fp32 result, so only that tree
+    # (evaluated here with exact rationals) matches, and every term counts.
+    from oracle.nvfp4 import _tree16
+    rng = np.random.default_rng(0)
+    e = (rng.uniform(1, 2, (400, 16)) * 2.0 ** rng.integers(-30, 30, (400, 16))).astype(F32)
+    got = _tree16(e)
+    for row, g_or in zip(e, got):
+        g = [exact(v) for v in row]
+        L = rn32(rn32(rn32(g[0] + g[8]) + rn32(g[4] + g[12])) + rn32(rn32(g[2] + g[10]) + rn32(g[6] + g[14])))
+        R = rn32(rn32(rn32(g[1] + g[9]) + rn32(g[5] + g[13])) + rn32(rn32(g[3] + g[11]) + rn32(g[7] + g[15])))
+        assert to_f32(rn32(L + R)) == g_or
+    # all sixteen terms enter: distinct powers of two sum exactly
+    p = (2.0 ** np.arange(16)).astype(F32)[None, :]
+    assert _tree16(p)[0] == F32(2 ** 16 - 1)

@@ -1,0 +1,135 @@
+// Global amax A = NaN-dropping max of |x'| (x' = x + residual), per tensor
+// or per row.  Four-over-six pull request, What: a scalar global_amax selects
+// per-tensor scaling and a (rows,) vector the row-wise variant; CuTe DSL
+// kernel Design: NaN-dropping max (an all-NaN set gives 0).
+//
+// Per tensor: two passes.  Pass 1 streams the tensor with 128-bit loads in a
+// grid-stride loop (each lane 16 elements per step), reduces inside the wave
+// with cross-lane max, then across the workgroup in LDS, and writes one
+// partial per workgroup into the caller's workspace.  Pass 2 (one workgroup)
+// reduces the partials and writes A.  Max is exact and order-free, so the
+// result does not depend on the launch geometry.  Per row: one workgroup per
+// row, same reductions.
+#include "nvfp4_device.hpp"
+#include "nvfp4_launch.hpp"
+
+namespace nvfp4 {
+
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxMaxGroups = 2048;
+
+NV_DEV float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Workgroup max of one value per lane; every lane gets the result.
+NV_DEV float block_max(float v, float* lds) {
+  v = wave_max(v);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  float r = 0.0f;
+  for (int i = 0; i < nw; ++i) r = fmaxf(r, lds[i]);
+  return r;
+}
+
+template <typename InT, bool HAS_RES>
+NV_DEV float group_absmax(const InT* x, const float* res, int64_t g) {
+  float xv[16];
+  load16(x + g * 16, xv);
+  if (HAS_RES) {
+    float r[16];
+    load16(res + g * 16, r);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xv[i] = xv[i] + r[i];
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xv[i]));
+  return a;
+}
+
+template <typename InT, bool HAS_RES>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_partial(const InT* __restrict__ x,
+                                                               const float* __restrict__ res,
+                                                               int64_t ngroups,
+                                                               float* __restrict__ partial) {
+  __shared__ float lds[kAmaxThreads / 64];
+  float a = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+  for (int64_t g = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; g < ngroups; g += stride)
+    a = fmaxf(a, group_absmax<InT, HAS_RES>(x, res, g));
+  a = block_max(a, lds);
+  if (threadIdx.x == 0) partial[blockIdx.x] = a;
+}
+
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_final(const float* __restrict__ partial,
+                                                             int n, float* __restrict__ out) {
+  __shared__ float lds[kAmaxThreads / 64];
+  float a = 0.0f;
+  for (int i = threadIdx.x; i < n; i += kAmaxThreads) a = fmaxf(a, partial[i]);
+  a = block_max(a, lds);
+  if (threadIdx.x == 0) out[0] = a;
+}
+
+template <typename InT, bool HAS_RES>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_rows(const InT* __restrict__ x,
+                                                            const float* __restrict__ res,
+                                                            int64_t M, int64_t K,
+                                                            float* __restrict__ out) {
+  __shared__ float lds[kAmaxThreads / 64];
+  const int64_t nbk = K / 16;
+  for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+    float a = 0.0f;
+    for (int64_t b = threadIdx.x; b < nbk; b += kAmaxThreads)
+      a = fmaxf(a, group_absmax<InT, HAS_RES>(x + m * K, HAS_RES ? res + m * K : res, b));
+    a = block_max(a, lds);
+    if (threadIdx.x == 0) out[m] = a;
+  }
+}
+
+static int64_t partial_groups(int64_t M, int64_t K) {
+  const int64_t ng = M * K / 16;
+  int64_t g = (ng + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
+  if (g < 1) g = 1;
+  if (g > kAmaxMaxGroups) g = kAmaxMaxGroups;
+  return g;
+}
+
+size_t amax_workspace_bytes(int64_t M, int64_t K) {
+  return (size_t)partial_groups(M, K) * sizeof(float);
+}
+
+template <typename InT>
+static int amax_typed(const InT* x, int64_t M, int64_t K, const float* res, int mode,
+                      float* out, float* ws, hipStream_t st) {
+  const int64_t ng = M * K / 16;
+  if (mode == 2) {
+    if (M == 0) return 0;
+    const unsigned grid = (unsigned)(M < 65536 ? M : 65536);
+    if (res) hipLaunchKernelGGL((k_amax_rows<InT, true>), dim3(grid), dim3(kAmaxThreads), 0, st, x, res, M, K, out);
+    else hipLaunchKernelGGL((k_amax_rows<InT, false>), dim3(grid), dim3(kAmaxThreads), 0, st, x, res, M, K, out);
+    return (int)hipGetLastError();
+  }
+  const int64_t groups = partial_groups(M, K);
+  if (ng > 0) {
+    if (res) hipLaunchKernelGGL((k_amax_partial<InT, true>), dim3((unsigned)groups), dim3(kAmaxThreads), 0, st, x, res, ng, ws);
+    else hipLaunchKernelGGL((k_amax_partial<InT, false>), dim3((unsigned)groups), dim3(kAmaxThreads), 0, st, x, res, ng, ws);
+  }
+  hipLaunchKernelGGL(k_amax_final, dim3(1), dim3(kAmaxThreads), 0, st, ws, ng > 0 ? (int)groups : 0, out);
+  return (int)hipGetLastError();
+}
+
+int launch_amax(const void* x, int in_bf16, int64_t M, int64_t K, const float* residual,
+                int mode, float* amax_out, void* workspace, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* ws = reinterpret_cast<float*>(workspace);
+  if (in_bf16)
+    return amax_typed(reinterpret_cast<const uint16_t*>(x), M, K, residual, mode, amax_out, ws, st);
+  return amax_typed(reinterpret_cast<const float*>(x), M, K, residual, mode, amax_out, ws, st);
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,153 @@
+// Device helpers shared by the NVFP4 kernels (gfx950 / CDNA4).
+//
+// Every floating-point operation here is one IEEE binary32 operation rounded
+// to nearest-even: the library is compiled with -ffp-contract=off (no fused
+// multiply-add unless written as fmaf), denormals are kept, and fp32
+// division and 1/x are the correctly rounded HIP defaults.  fminf / fmaxf are
+// the NaN-dropping IEEE minNum / maxNum.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define NV_DEV __device__ __forceinline__
+
+namespace nvfp4 {
+
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+constexpr float kE4m3Max = 448.0f;
+
+NV_DEV float bits2f(uint32_t u) { return __uint_as_float(u); }
+NV_DEV uint32_t f2bits(float f) { return __float_as_uint(f); }
+
+// ---------------------------------------------------------------- formats
+
+// e4m3 (OCP E4M3FN) byte of a scale sigma in [0, inf) (not NaN): round to
+// nearest, ties to even, saturating at 0x7E = 448.  Below 2^-6 the format is
+// subnormal with step 2^-9, so the code is sigma * 2^9 rounded to an integer
+// (0..8; 8 is the first normal code 0x08).  Above, the fp32 mantissa is
+// rounded to 3 bits on the bit pattern and the exponent rebased from 127 to 7.
+NV_DEV uint32_t e4m3_encode(float sigma) {
+  if (sigma < 0x1p-6f) return (uint32_t)__builtin_rintf(sigma * 512.0f);
+  uint32_t b = f2bits(sigma);
+  uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  uint32_t code = (r >> 20) - (120u << 3);
+  return code < 0x7Eu ? code : 0x7Eu;
+}
+
+// e4m3 byte (0..0x7E) -> value: subnormal m * 2^-9, else (1 + m/8) 2^(e-7).
+NV_DEV float e4m3_decode(uint32_t c) {
+  uint32_t e = c >> 3, m = c & 7u;
+  return e ? bits2f(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// Round-to-nearest-even of a magnitude v >= 0 onto the e2m1 grid
+// {0,.5,1,1.5,2,3,4,6}, saturating at 6 (a NaN v gives 6; the caller clears
+// its sign).  The grid has step 0.5 below 2, 1 on [2,4) and 2 on [4,6]; the
+// value is scaled so the step is 1, rounded to an integer with ties to even
+// (which is ties to the even code), and mapped back.  Returns the magnitude
+// index 0..7 and the grid value q.
+NV_DEV uint32_t e2m1_rtn(float v, float& q) {
+  v = fminf(v, 6.0f);
+  float mul, step;
+  uint32_t off;
+  if (v < 2.0f) { mul = 2.0f; step = 0.5f; off = 0; }
+  else if (v < 4.0f) { mul = 1.0f; step = 1.0f; off = 2; }
+  else { mul = 0.5f; step = 2.0f; off = 4; }
+  float n = __builtin_rintf(v * mul);
+  q = n * step;
+  return (uint32_t)n + off;
+}
+
+// Stochastic rounding of a magnitude v >= 0 onto the e2m1 grid: between the
+// grid points lo <= v < hi the value rounds up iff u < (v - lo) / (hi - lo),
+// u = u16 * 2^-16.  In the scaled domain t = v * mul the step is 1, so
+// lo = floor(t) and the fraction t - floor(t) is exact.  v >= 6 (or NaN)
+// saturates to 6 with no draw.
+NV_DEV uint32_t e2m1_sr(float v, uint32_t u16, float& q) {
+  if (!(v < 6.0f)) { q = 6.0f; return 7u; }
+  float mul, step;
+  uint32_t off;
+  if (v < 2.0f) { mul = 2.0f; step = 0.5f; off = 0; }
+  else if (v < 4.0f) { mul = 1.0f; step = 1.0f; off = 2; }
+  else { mul = 0.5f; step = 2.0f; off = 4; }
+  float t = v * mul;
+  float n = floorf(t);
+  float f = t - n;
+  float u = (float)u16 * 0x1p-16f;
+  if (u < f) n = n + 1.0f;
+  q = n * step;
+  return (uint32_t)n + off;
+}
+
+// fp32 -> bf16 bits, round-to-nearest-even; NaN -> 0x7FC0.
+NV_DEV uint32_t f32_to_bf16(float f) {
+  uint32_t u = f2bits(f);
+  uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (f != f) ? 0x7FC0u : r;
+}
+
+// ------------------------------------------------------------------- RNG
+// Jarzynski & Olano, "Hash Functions for GPU Rendering" (JCGT 2020), the
+// "pcg" hash: one PCG32 LCG step, then the RXS-M-XS output permutation.
+__host__ __device__ inline uint32_t pcg_hash(uint32_t v) {
+  uint32_t state = v * 747796405u + 2891336453u;
+  uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+  return (word >> 22u) ^ word;
+}
+
+// Per-call key of the (seed, step) stream.
+inline uint32_t rng_key_host(uint32_t seed, uint32_t step) {
+  return pcg_hash(seed ^ pcg_hash(step ^ 0x9E3779B9u));
+}
+
+// ----------------------------------------------------------------- loads
+
+// 16 consecutive bf16 (32 bytes, 16-byte aligned) -> fp32 (exact).
+NV_DEV void load16(const uint16_t* p, float x[16]) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  uint4 a = q[0], b = q[1];
+  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = bits2f(w[i] << 16);
+    x[2 * i + 1] = bits2f(w[i] & 0xFFFF0000u);
+  }
+}
+
+// 16 consecutive fp32 (64 bytes, 16-byte aligned).
+NV_DEV void load16(const float* p, float x[16]) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float4 v = q[i];
+    x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+  }
+}
+
+NV_DEV void store16(float* p, const float x[16]) {
+  float4* q = reinterpret_cast<float4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+}
+
+NV_DEV void store16_bf16(uint16_t* p, const float x[16]) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = f32_to_bf16(x[2 * i]) | (f32_to_bf16(x[2 * i + 1]) << 16);
+  uint4* q = reinterpret_cast<uint4*>(p);
+  q[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  q[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+// Global scale from amax A and D = 6 * bound: S_enc = min(D / A, FLT_MAX),
+// S_dec = A / D (true divisions).
+NV_DEV void global_scales(float A, float D, float& S_enc, float& S_dec) {
+  S_enc = fminf(D / A, kFltMax);
+  S_dec = A / D;
+}
+
+// Encode reciprocal rho = min(1 / (s * S_dec), FLT_MAX).
+NV_DEV float encode_reciprocal(float s, float S_dec) { return fminf(1.0f / (s * S_dec), kFltMax); }
+
+}  // namespace nvfp4

@@ -1,0 +1,187 @@
+/*
+ * nvfp4.h - C ABI of libnvfp4, NVFP4 block quantization for AMD CDNA4 (gfx950).
+ *
+ * NVFP4: 4-bit e2m1 element codes (sign bit + magnitude grid
+ * {0, .5, 1, 1.5, 2, 3, 4, 6}) packed two per byte, one e4m3 scale byte per
+ * 16-element block, and an optional fp32 second-level (global) scale derived
+ * from a global amax.  Sources: the "fp4-train" kernel card (Method, API,
+ * Requirements and limits), the four-over-six pull request "Add NVFP4
+ * four-over-six (row-wise) quantization to the training prototype" (What,
+ * numeric details, CuTe DSL kernel Design) and "Stable FP4 Training via
+ * Transposition-Invariant Block Quantization" (abstract).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense row-major [M, K] with K % 16 == 0 ("K a multiple of 16;
+ *   float32 or bfloat16 input", fp4-train, Requirements and limits).  Element
+ *   (m, k) has the global index i = m*K + k; M*K must not exceed 2^33 so that
+ *   the pair index i >> 1 of the random-number generator fits 32 bits.
+ * - All pointers are DEVICE pointers, owned by the caller, allocated on the
+ *   device that is current when the call is made.  The library allocates no
+ *   memory and keeps no state; calls are asynchronous on `stream` (a
+ *   hipStream_t; NULL is the default stream) and return once the kernels are
+ *   queued.  Outputs must not overlap inputs, except that nvfp4_qdq may
+ *   write `out` over `x` when both have the same dtype.
+ * - Alignment: x, residual and out must be 16-byte aligned; packed codes
+ *   8-byte aligned; scale bytes and amax pointers need 4-byte alignment
+ *   only where stated.
+ * - Layouts: packed codes [M, K/2] bytes, byte j of a row holds element 2j in
+ *   its low nibble and element 2j+1 in its high nibble; code = sign << 3 |
+ *   magnitude index.  Scales [M, K/16] e4m3 bytes (plain row-major, no
+ *   tensor-core swizzle).  16x16 tile scales [M/16, K/16].
+ * - Errors: every argument is validated on the host before anything is
+ *   launched; on error nothing is written and a status other than NVFP4_OK is
+ *   returned.  NVFP4_E_HIP reports a failed kernel launch.  Nothing is
+ *   printed and nothing aborts.  An empty tensor (M == 0 or K == 0) returns
+ *   NVFP4_OK and launches nothing, except that nvfp4_amax writes 0.
+ *
+ * Numerics (identical on every path; the CPU oracle is the reference)
+ * - x' = x + r when a residual r is given (error feedback), one fp32 add.
+ * - Block amax a = NaN-dropping max of |x'| (all-NaN block -> 0).
+ * - Global scale from amax A and bound B (448, or 256/448 for four-over-six):
+ *   D = 6*B, S_enc = min(D / A, FLT_MAX), S_dec = A / D, true fp32 divisions.
+ * - e4m3 scale: sigma -> min(sigma, 448) -> round-to-nearest-even, satfinite;
+ *   s = decoded scale; encode reciprocal rho = min(1 / (s * S_dec), FLT_MAX).
+ * - Element: v = |x'| * rho, rounded to the e2m1 grid (RTN: nearest, ties to
+ *   even; SR: up with probability equal to the fractional distance), >= 6
+ *   saturates, a NaN v encodes +6 (0x7); sign bit from x'.
+ * - Dequantize: x_hat = (val * s) * S_dec in fp32, then bf16 round-to-nearest-
+ *   even (NaN -> 0x7FC0) when the output is bf16.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_E_NULL = 1,   /* a required pointer is NULL */
+  NVFP4_E_SHAPE = 2,  /* negative size, K % 16 != 0, or M % 16 != 0 where tiles need it */
+  NVFP4_E_DTYPE = 3,  /* unknown dtype code */
+  NVFP4_E_ALIGN = 4,  /* a pointer misses its required alignment */
+  NVFP4_E_ARG = 5,    /* bad enum value, bound, or workspace too small */
+  NVFP4_E_RANGE = 6,  /* M*K > 2^33 */
+  NVFP4_E_HIP = 7     /* the HIP runtime rejected a launch */
+} nvfp4_status;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_BF16 = 1 } nvfp4_dtype;
+typedef enum { NVFP4_RTN = 0, NVFP4_SR = 1 } nvfp4_round;
+typedef enum { NVFP4_MAE = 0, NVFP4_MSE = 1 } nvfp4_err;
+/* Second-level scale: none, one amax for the tensor, or one amax per row. */
+typedef enum { NVFP4_SCALE_NONE = 0, NVFP4_SCALE_TENSOR = 1, NVFP4_SCALE_ROW = 2 } nvfp4_scale_mode;
+
+/* Human-readable name of a status (static string, never NULL). */
+const char* nvfp4_status_str(nvfp4_status s);
+
+/* Bytes of workspace nvfp4_amax needs for a per-tensor amax of M*K elements. */
+size_t nvfp4_amax_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * nvfp4_amax - global amax A = NaN-dropping max of |x'| (x' = x + residual
+ * when residual != NULL), over the whole tensor (mode TENSOR: amax_out[0],
+ * two passes: per-workgroup partials into `workspace`, then one reduction)
+ * or over each row (mode ROW: amax_out[0..M-1], one pass).  Source: the
+ * four-over-six pull request, What (scalar global_amax = per-tensor
+ * scaling, a (rows,) vector = row-wise) and CuTe DSL kernel Design
+ * (NaN-dropping max).  workspace: device buffer of at least
+ * nvfp4_amax_workspace_bytes(M, K) bytes (TENSOR only; may be NULL for
+ * ROW).  An empty tensor gives 0.
+ */
+nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
+                        const float* residual, nvfp4_scale_mode mode, float* amax_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_quantize - NVFP4 quantize on 1x16 blocks (fp4-train, API
+ * quantize(x, stochastic, residual, seed, step); Method).
+ *   x        [M, K] fp32 or bf16 (dt).
+ *   residual NULL, or [M, K] fp32 error-feedback residual updated in place:
+ *            x' = x + r, then r <- x' - x_hat with the fp32 dequantized x_hat.
+ *   global_amax NULL (block scale = block_absmax / 6, fp4-train Method), or
+ *            a device pointer to one fp32 amax A: standard NVFP4 two-level
+ *            scaling with bound 448, sigma = a * (S_enc * (1/6)).
+ *   rnd, seed, step: NVFP4_RTN, or NVFP4_SR with the counter-based
+ *            generator keyed by (seed, step) and the global element index.
+ *   packed   [M, K/2] out; scales [M, K/16] out.
+ */
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
+                            float* residual, const float* global_amax, nvfp4_round rnd,
+                            uint32_t seed, uint32_t step, uint8_t* packed, uint8_t* scales,
+                            void* stream);
+
+/*
+ * nvfp4_dequantize - NVFP4 -> bf16 or fp32 (fp4-train, API dequantize(packed,
+ * scale, M, K) -> bf16).  x_hat = (val * s) * S_dec.
+ *   tile16   0: scales [M, K/16] (1x16 blocks); 1: tile scales [M/16, K/16]
+ *            (M % 16 == 0).
+ *   global_amax, scale_mode, bound: the producer's second-level scale: mode
+ *            NONE (global_amax ignored, S_dec = 1), TENSOR (global_amax[0]) or
+ *            ROW (global_amax[0..M-1], 1x16 only); bound 448 (standard, 2D) or
+ *            256/448 (four-over-six).
+ *   out      [M, K] of out_dt.
+ */
+nvfp4_status nvfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t M,
+                              int64_t K, int tile16, const float* global_amax,
+                              nvfp4_scale_mode scale_mode, float bound, void* out,
+                              nvfp4_dtype out_dt, void* stream);
+
+/*
+ * nvfp4_qdq - quantize then dequantize in one pass, "the value the tensor
+ * cores use" (fp4-train, API qdq(x, stochastic, residual, seed, step)).
+ * Arguments as nvfp4_quantize; out [M, K] of out_dt (bf16 as in the card);
+ * packed_opt / scales_opt: NULL, or also receive the codes and scales.
+ * With a residual this is one error-feedback step (fp4-train, Method).
+ */
+nvfp4_status nvfp4_qdq(const void* x, nvfp4_dtype dt, int64_t M, int64_t K, float* residual,
+                       const float* global_amax, nvfp4_round rnd, uint32_t seed,
+                       uint32_t step, void* out, nvfp4_dtype out_dt, uint8_t* packed_opt,
+                       uint8_t* scales_opt, void* stream);
+
+/*
+ * nvfp4_quantize_4over6 - four-over-six NVFP4 quantize on 1x16 blocks (the
+ * four-over-six pull request, What: four_over_six_quantize(x, global_amax,
+ * block, err_mode, e4m3_scale_bound); numeric details; CuTe DSL kernel
+ * Design).  Each block is encoded with sigma6 = (a / 6) * S_enc (map-to-6)
+ * and sigma4 = sigma6 * 1.5 (map-to-4), RTN only; the candidate whose
+ * dequantization error sum_i |x_i - d_i| (MAE) or sum_i (x_i - d_i)^2 (MSE),
+ * d_i = ((val_i * s) * A) / (6*bound), accumulated in element order 0..15, is
+ * strictly lower is kept; ties and NaN keep map-to-6.
+ *   global_amax  mode TENSOR: global_amax[0] is read.  mode ROW: one amax
+ *                per row; if amax_is_input != 0 they are read from
+ *                global_amax[0..M-1], otherwise the kernel computes each
+ *                row's NaN-dropping amax in the same pass and writes it there.
+ *   err          NVFP4_MAE or NVFP4_MSE.   bound  256 or 448.
+ *   packed [M, K/2], scales [M, K/16] out.
+ */
+nvfp4_status nvfp4_quantize_4over6(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
+                                   float* global_amax, nvfp4_scale_mode mode,
+                                   int amax_is_input, nvfp4_err err, float bound,
+                                   uint8_t* packed, uint8_t* scales, void* stream);
+
+/*
+ * nvfp4_quantize_2d - transposition-invariant 2D NVFP4 ("Stable FP4 Training
+ * via Transposition-Invariant Block Quantization", abstract: one scale per
+ * 16x16 tile shared by the forward and transposed operands, combined with
+ * stochastic rounding).  M % 16 == 0.  Every element is encoded once (its
+ * random draw keyed by its row-major index in X); the rowwise codes are
+ * written to packed_row [M, K/2] and the same codes transposed to
+ * packed_col [K, M/2] (NULL to skip), so packed_col is the rowwise packing of
+ * Q(X)^T.  Block scale: a/6 without a global scale; with global_amax (one
+ * fp32 amax) the standard sigma = a * (S_enc * (1/6)), bound 448.
+ * tile_scales [M/16, K/16] out.
+ */
+nvfp4_status nvfp4_quantize_2d(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
+                               const float* global_amax, nvfp4_round rnd, uint32_t seed,
+                               uint32_t step, uint8_t* packed_row, uint8_t* packed_col,
+                               uint8_t* tile_scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -147,7 +147,7 @@ def amax(x, residual=None, mode="tensor"):
     (rows,) vector the row-wise variant."""
     xp = _ef_add(_to_f32(x), residual)
     if mode == "tensor":
-        return _nan_drop_absmax(xp.reshape(-1), axis=0) if xp.size else F32(0.0)
+        return F32(_nan_drop_absmax(xp.reshape(-1), axis=0)) if xp.size else F32(0.0)
     if mode == "row":
         return _nan_drop_absmax(xp, axis=1)
     raise ValueError(mode)

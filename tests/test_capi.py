@@ -1,0 +1,83 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/nvfp4.h declares, and rejects bad arguments on the host with the
+documented status before anything is launched (fake, never-dereferenced
+device addresses are passed; no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_block_quantization_nvfp4_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "nvfp4.h")
+A = 1 << 20  # a fake, 256-byte-aligned device address (never dereferenced)
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared()
+    assert {"nvfp4_quantize", "nvfp4_dequantize", "nvfp4_qdq", "nvfp4_quantize_4over6",
+            "nvfp4_quantize_2d", "nvfp4_amax"} <= set(names)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES)
+
+
+def test_status_strings():
+    for s in range(8):
+        assert L.status_str(s)
+    assert L.status_str(99) == "unknown status"
+
+
+def q(*, x=A, dt=L.BF16, M=32, K=64, res=None, ga=None, rnd=L.RTN, packed=A, scales=A):
+    return L.lib().nvfp4_quantize(x, dt, M, K, res, ga, rnd, 0, 0, packed, scales, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=24), L.E_SHAPE), (dict(M=-1), L.E_SHAPE), (dict(K=-16), L.E_SHAPE),
+    (dict(dt=7), L.E_DTYPE), (dict(rnd=5), L.E_ARG), (dict(x=None), L.E_NULL),
+    (dict(packed=None), L.E_NULL), (dict(scales=None), L.E_NULL),
+    (dict(x=A + 8), L.E_ALIGN), (dict(res=A + 4), L.E_ALIGN), (dict(packed=A + 4), L.E_ALIGN),
+    (dict(ga=A + 2), L.E_ALIGN), (dict(M=1 << 22, K=1 << 12), L.E_RANGE),
+])
+def test_quantize_rejects(kw, status):
+    assert q(**kw) == status
+
+
+def test_empty_is_ok_without_pointers():
+    assert q(x=None, packed=None, scales=None, M=0) == L.OK
+    assert q(x=None, packed=None, scales=None, K=0) == L.OK
+
+
+def test_other_entry_points_reject():
+    lib = L.lib()
+    # dequantize: tile16 needs M % 16; bad bound with a global scale; NULL out
+    assert lib.nvfp4_dequantize(A, A, 8, 32, 1, None, 0, 448.0, A, L.BF16, None) == L.E_SHAPE
+    assert lib.nvfp4_dequantize(A, A, 16, 32, 0, A, 1, 300.0, A, L.BF16, None) == L.E_ARG
+    assert lib.nvfp4_dequantize(A, A, 16, 32, 0, None, 0, 448.0, None, L.BF16, None) == L.E_NULL
+    assert lib.nvfp4_dequantize(A, A, 16, 32, 1, A, 2, 448.0, A, L.BF16, None) == L.E_ARG
+    # qdq: bad out dtype
+    assert lib.nvfp4_qdq(A, L.BF16, 4, 32, None, None, 0, 0, 0, A, 9, None, None, None) == L.E_DTYPE
+    assert lib.nvfp4_qdq(A, L.BF16, 4, 32, None, None, 0, 0, 0, A, L.BF16, A, None, None) == L.E_NULL
+    # four-over-six: bound, err, mode, per-tensor must be given
+    assert lib.nvfp4_quantize_4over6(A, L.BF16, 4, 32, A, 1, 1, 0, 300.0, A, A, None) == L.E_ARG
+    assert lib.nvfp4_quantize_4over6(A, L.BF16, 4, 32, A, 1, 1, 3, 256.0, A, A, None) == L.E_ARG
+    assert lib.nvfp4_quantize_4over6(A, L.BF16, 4, 32, A, 0, 1, 0, 256.0, A, A, None) == L.E_ARG
+    assert lib.nvfp4_quantize_4over6(A, L.BF16, 4, 32, A, 1, 0, 0, 256.0, A, A, None) == L.E_ARG
+    assert lib.nvfp4_quantize_4over6(A, L.BF16, 4, 32, None, 2, 0, 0, 256.0, A, A, None) == L.E_NULL
+    # 2D: M % 16
+    assert lib.nvfp4_quantize_2d(A, L.BF16, 24, 32, None, 0, 0, 0, A, A, A, None) == L.E_SHAPE
+    assert lib.nvfp4_quantize_2d(A, L.BF16, 32, 32, None, 0, 0, 0, None, A, A, None) == L.E_NULL
+    # amax: workspace too small / missing, bad mode
+    need = lib.nvfp4_amax_workspace_bytes(1024, 1024)
+    assert need >= 4
+    assert lib.nvfp4_amax(A, L.BF16, 1024, 1024, None, 1, A, A, need - 1, None) == L.E_ARG
+    assert lib.nvfp4_amax(A, L.BF16, 1024, 1024, None, 1, A, None, need, None) == L.E_NULL
+    assert lib.nvfp4_amax(A, L.BF16, 1024, 1024, None, 0, A, A, need, None) == L.E_ARG

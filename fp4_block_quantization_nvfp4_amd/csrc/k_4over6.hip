@@ -112,6 +112,306 @@ __global__ __launch_bounds__(k46MaxThreads) void k_4over6(const InT* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row-per-workgroup kernel for bf16 input (K <= 16384).  Same numerics as
+// above, with three exact rewrites of the per-element work:
+//  * e2m1 encode by the gfx950 packed fp32 -> fp4 conversion (scale 1.0),
+//    which rounds to nearest-even and saturates at +-6 exactly like the
+//    software encoder for every finite and infinite input (checked on all
+//    2^32 fp32 values); it differs only for negative NaN, so blocks holding a
+//    NaN or an infinity take the software path.
+//  * The error-path dequant d = ((val * s) * A) / D depends only on the
+//    block's scale code and the code's magnitude, so the workgroup builds a
+//    table of d (and of the encode reciprocals rho) in LDS once per row, for
+//    the span of scale codes the row uses; an element's d is one LDS read.
+//    The block scale bytes come from the hardware fp32 -> e4m3 conversion,
+//    which equals the software round-to-nearest-even encoder on every fp32
+//    value in [0, 448] (checked exhaustively).
+//  * Divisions by 6 and by D use reciprocal-multiply plus one exact FMA
+//    remainder correction, which is correctly rounded for every float32
+//    numerator of magnitude >= 2^-117 (verified exhaustively on the host);
+//    smaller numerators take the true division.
+// A two-wave workgroup owns one row: it loads the row (R blocks per lane)
+// into registers, reduces the row amax, builds the tables, then encodes its
+// blocks.
+
+typedef unsigned short nv_us2 __attribute__((ext_vector_type(2)));
+
+NV_DEV float div_fast(float n, float D, float rD) {
+  const float q0 = n * rD;
+  const float rem = __builtin_fmaf(-q0, D, n);
+  return __builtin_fmaf(rem, rD, q0);
+}
+
+NV_DEV float div_guarded(float n, float D, float rD) {
+  const uint32_t e = (f2bits(n) >> 23) & 0xFFu;
+  if (e >= 10u && e <= 254u) return div_fast(n, D, rD);
+  return n / D;
+}
+
+// Max of the 16 bf16 magnitudes of a block as 16-bit patterns (for
+// non-NaN values the integer order is the value order; a NaN compares above
+// every finite value and infinity).
+NV_DEV uint32_t absmax_bits(const uint4 r0, const uint4 r1) {
+  const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  nv_us2 m = __builtin_bit_cast(nv_us2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(nv_us2, w[i] & 0x7FFF7FFFu));
+  return m.x > m.y ? m.x : m.y;
+}
+
+// NaN-dropping variant (the block holds a NaN): max over non-NaN magnitudes.
+NV_DEV uint32_t absmax_bits_nan_drop(const uint4 r0, const uint4 r1) {
+  const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0x7FFFu;
+    if (h <= 0x7F80u && h > m) m = h;
+  }
+  return m;
+}
+
+NV_DEV void unpack16(const uint4 r0, const uint4 r1, float xv[16]) {
+  const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    xv[2 * i] = bits2f(w[i] << 16);
+    xv[2 * i + 1] = bits2f(w[i] & 0xFFFF0000u);
+  }
+}
+
+NV_DEV float e2m1_value(uint32_t m) {
+  return m <= 4u ? (float)m * 0.5f : (m == 5u ? 3.0f : (m == 6u ? 4.0f : 6.0f));
+}
+
+constexpr int kDStride = 9;  // floats per scale code in the d table (8 used; 9 spreads LDS banks)
+constexpr int kTabFloats = 128 + 127 * kDStride;  // rho[128] then d[127][kDStride]
+
+// Lane-wise max of two packed pairs of u16.
+NV_DEV uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(nv_us2, a),
+                                                                 __builtin_bit_cast(nv_us2, b)));
+}
+
+// Wave-wide max of two packed u16 values, returned to every lane (uniform):
+// quad permutations, half-row and row mirrors (DPP, no LDS), then the four
+// 16-lane rows are combined through lane reads.
+NV_DEV uint32_t wave_max_pk_u16(uint32_t v) {
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row half mirror
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return pk_max_u16(pk_max_u16(r0, r1), pk_max_u16(r2, r3));
+}
+
+// Error sum of one candidate over a block, in element order: t points at the
+// candidate's row of the d table, c[2] holds its 16 codes; element i's d is
+// entry (code & 7).
+template <bool MSE>
+NV_DEV float error_sum(const float xv[16], const float* t, const uint32_t c[2]) {
+  const char* tb = reinterpret_cast<const char*>(t);
+  float E = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    // 4 * (code & 7) of the even / odd elements, one byte each.  The empty
+    // asm keeps the compiler from re-deriving per-element shifts, so each
+    // lookup is one add with a byte-select operand.
+    uint32_t ev = (c[w] << 2) & 0x1C1C1C1Cu;
+    uint32_t od = (c[w] >> 2) & 0x1C1C1C1Cu;
+    asm("" : "+v"(ev), "+v"(od));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float d0 = *reinterpret_cast<const float*>(tb + ((ev >> (8 * b)) & 0xFFu));
+      const float d1 = *reinterpret_cast<const float*>(tb + ((od >> (8 * b)) & 0xFFu));
+      const float u0 = fabsf(xv[8 * w + 2 * b]) - d0;
+      const float u1 = fabsf(xv[8 * w + 2 * b + 1]) - d1;
+      const float e0 = MSE ? u0 * u0 : fabsf(u0);
+      const float e1 = MSE ? u1 * u1 : fabsf(u1);
+      E = (w == 0 && b == 0) ? e0 : E + e0;
+      E = E + e1;
+    }
+  }
+  return E;
+}
+
+template <int SEL>
+NV_DEV void cvt_pair(uint32_t& c, float a, float b) {
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, a, b, 1.0f, SEL);
+}
+
+// Codes of one candidate: v = x * rho, rounded to e2m1 by the hardware
+// conversion, two elements per instruction, even element in the low nibble.
+NV_DEV void encode16_hw(const float xv[16], float rho, uint32_t c[2]) {
+  c[0] = 0u;
+  c[1] = 0u;
+  cvt_pair<0>(c[0], xv[0] * rho, xv[1] * rho);
+  cvt_pair<1>(c[0], xv[2] * rho, xv[3] * rho);
+  cvt_pair<2>(c[0], xv[4] * rho, xv[5] * rho);
+  cvt_pair<3>(c[0], xv[6] * rho, xv[7] * rho);
+  cvt_pair<0>(c[1], xv[8] * rho, xv[9] * rho);
+  cvt_pair<1>(c[1], xv[10] * rho, xv[11] * rho);
+  cvt_pair<2>(c[1], xv[12] * rho, xv[13] * rho);
+  cvt_pair<3>(c[1], xv[14] * rho, xv[15] * rho);
+}
+
+// A block takes the table-free software path when it holds a NaN or an
+// infinity, is all zero, or has an amax so small that a / 6 leaves the range
+// where the fast division is verified.
+NV_DEV bool slow_block(uint32_t ab) { return ab >= 0x7F80u || ab < 0x0500u; }
+
+// One workgroup of kRowThreads lanes (two waves) per row; lane t owns blocks
+// t, t + kRowThreads, ... (R per lane).  Reductions run inside each wave with
+// DPP and lane reads, then across the two waves through LDS; three workgroup
+// barriers per row (row amax, span of scale codes, tables built).
+constexpr int kRowThreads = 128;
+
+template <bool MSE, int MODE, int R>
+__global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __restrict__ x,
+                                                             float* __restrict__ amax, float D,
+                                                             int64_t M, int64_t K,
+                                                             uint8_t* __restrict__ packed,
+                                                             uint8_t* __restrict__ scales) {
+  __shared__ __attribute__((aligned(32))) float tab[kTabFloats];
+  __shared__ uint32_t red[2][kRowThreads / 64];
+  float* rhoT = tab;
+  float* dT = tab + 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int nbk = (int)(K >> 4);
+  const uint16_t* xr = x + row * K;
+
+  uint4 raw[R][2];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int b = tid + kRowThreads * j;
+    if (b < nbk) {
+      const uint4* p = reinterpret_cast<const uint4*>(xr + (int64_t)b * 16);
+      raw[j][0] = p[0];
+      raw[j][1] = p[1];
+    } else {
+      raw[j][0] = make_uint4(0, 0, 0, 0);
+      raw[j][1] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  // info[j]: bits 0..15 the block's bf16 absmax pattern (NaN included),
+  // then bits 16..31 the two scale codes.
+  uint32_t info[R];
+  uint32_t lane_max = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    info[j] = absmax_bits(raw[j][0], raw[j][1]);
+    const uint32_t ab = info[j] > 0x7F80u ? absmax_bits_nan_drop(raw[j][0], raw[j][1]) : info[j];
+    lane_max = ab > lane_max ? ab : lane_max;
+  }
+
+  float A;
+  if (MODE == 1) {
+    A = amax[0];
+  } else if (MODE == 2) {
+    A = amax[row];
+  } else {
+    const uint32_t wm = wave_max_pk_u16(lane_max);
+    if (lane == 0) red[0][wave] = wm;
+    __syncthreads();
+    const uint32_t m = pk_max_u16(red[0][0], red[0][1]);
+    A = bits2f((m & 0xFFFFu) << 16);
+    if (tid == 0) amax[row] = A;
+  }
+  float S_enc, S_dec;
+  global_scales(A, D, S_enc, S_dec);
+
+  // Scale codes of both candidates per block (hardware e4m3 conversion,
+  // round-to-nearest-even; sigma is capped to [0, 448] first) and the span of
+  // codes used by the row's fast blocks, reduced as (255 - kmin, kmax).
+  uint32_t span = 0u;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const float a = bits2f(info[j] << 16);
+    const float sig6r = div_fast(a, 6.0f, 1.0f / 6.0f) * S_enc;
+    const float sig4r = sig6r * 1.5f;
+    const uint32_t kk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(sig6r, kE4m3Max),
+                                                                  fminf(sig4r, kE4m3Max), 0, false);
+    const bool fast = (tid + kRowThreads * j < nbk) && !slow_block(info[j]);
+    if (fast) span = pk_max_u16(span, ((0xFFu - (kk & 0xFFu)) << 16) | ((kk >> 8) & 0xFFu));
+    info[j] |= kk << 16;
+  }
+  const uint32_t ws = wave_max_pk_u16(span);
+  if (lane == 0) red[1][wave] = ws;
+  __syncthreads();
+  const uint32_t sp = pk_max_u16(red[1][0], red[1][1]);
+  const int kmin = 0xFF - (int)(sp >> 16), kmax = (int)(sp & 0xFFFFu);
+
+  if (kmin <= kmax) {
+    const float rD = 1.0f / D;
+    for (int k = kmin + tid; k <= kmax; k += kRowThreads)
+      rhoT[k] = encode_reciprocal(e4m3_decode((uint32_t)k), S_dec);
+    const float qm = e2m1_value((uint32_t)(tid & 7));
+    const int n = (kmax - kmin + 1) * 8;
+    for (int e = tid; e < n; e += kRowThreads) {
+      const uint32_t k = (uint32_t)kmin + (uint32_t)(e >> 3);
+      dT[k * kDStride + (e & 7)] = div_guarded((qm * e4m3_decode(k)) * A, D, rD);
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int b = tid + kRowThreads * j;
+    if (b >= nbk) continue;
+    const int64_t blk = row * nbk + b;
+    float xv[16];
+    unpack16(raw[j][0], raw[j][1], xv);
+    const uint32_t ab = info[j] & 0xFFFFu;
+    uint2 out;
+    uint32_t sbyte;
+    if (slow_block(ab)) {
+      const float a = bits2f((ab > 0x7F80u ? absmax_bits_nan_drop(raw[j][0], raw[j][1]) : ab) << 16);
+      const float sig6r = (a / 6.0f) * S_enc;
+      const float sig4r = sig6r * 1.5f;
+      const uint32_t k6 = e4m3_encode(fminf(sig6r, kE4m3Max));
+      const uint32_t k4 = e4m3_encode(fminf(sig4r, kE4m3Max));
+      const float s6 = e4m3_decode(k6), s4 = e4m3_decode(k4);
+      uint32_t a0, a1, b0, b1;
+      const float E6 = candidate<MSE>(xv, s6, encode_reciprocal(s6, S_dec), A, D, a0, a1);
+      const float E4 = candidate<MSE>(xv, s4, encode_reciprocal(s4, S_dec), A, D, b0, b1);
+      const bool pick4 = E4 < E6;
+      out = pick4 ? make_uint2(b0, b1) : make_uint2(a0, a1);
+      sbyte = pick4 ? k4 : k6;
+    } else {
+      const uint32_t k6 = (info[j] >> 16) & 0xFFu, k4 = info[j] >> 24;
+      uint32_t c6[2], c4[2];
+      encode16_hw(xv, rhoT[k6], c6);
+      encode16_hw(xv, rhoT[k4], c4);
+      const float E6 = error_sum<MSE>(xv, dT + k6 * kDStride, c6);
+      const float E4 = error_sum<MSE>(xv, dT + k4 * kDStride, c4);
+      const bool pick4 = E4 < E6;
+      out = pick4 ? make_uint2(c4[0], c4[1]) : make_uint2(c6[0], c6[1]);
+      sbyte = pick4 ? k4 : k6;
+    }
+    reinterpret_cast<uint2*>(packed)[blk] = out;
+    scales[blk] = (uint8_t)sbyte;
+  }
+}
+
+template <bool MSE, int MODE>
+static int launch_rows_R(int R, const uint16_t* x, float* amax, float D, int64_t M, int64_t K,
+                         uint8_t* packed, uint8_t* scales, hipStream_t st) {
+  const dim3 grid((unsigned)M), block(kRowThreads);
+#define NV46_CASE(RR) \
+  case RR: hipLaunchKernelGGL((k_4over6_rows<MSE, MODE, RR>), grid, block, 0, st, x, amax, D, M, K, packed, scales); break;
+  switch (R) {
+    NV46_CASE(1) NV46_CASE(2) NV46_CASE(3) NV46_CASE(4) NV46_CASE(5) NV46_CASE(6) NV46_CASE(7) NV46_CASE(8)
+    default: return (int)hipErrorInvalidValue;
+  }
+#undef NV46_CASE
+  return (int)hipGetLastError();
+}
+
 template <typename InT, bool MSE>
 static int launch46_mode(const InT* x, float* amax, int mode, int amax_is_input, float D,
                          int64_t M, int64_t K, uint8_t* packed, uint8_t* scales, hipStream_t st) {
@@ -135,6 +435,20 @@ int launch_4over6(const void* x, int in_bf16, int64_t M, int64_t K, float* amax,
   if (M == 0 || K == 0) return 0;
   const float D = 6.0f * bound;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t nbk = K / 16;
+  if (in_bf16 && nbk <= kRowThreads * 8 && M <= 0x7FFFFFFF) {
+    const int R = (int)((nbk + kRowThreads - 1) / kRowThreads);
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    const int md = mode == 1 ? 1 : (amax_is_input ? 2 : 3);
+    if (mse) {
+      if (md == 1) return launch_rows_R<true, 1>(R, xb, amax, D, M, K, packed, scales, st);
+      if (md == 2) return launch_rows_R<true, 2>(R, xb, amax, D, M, K, packed, scales, st);
+      return launch_rows_R<true, 3>(R, xb, amax, D, M, K, packed, scales, st);
+    }
+    if (md == 1) return launch_rows_R<false, 1>(R, xb, amax, D, M, K, packed, scales, st);
+    if (md == 2) return launch_rows_R<false, 2>(R, xb, amax, D, M, K, packed, scales, st);
+    return launch_rows_R<false, 3>(R, xb, amax, D, M, K, packed, scales, st);
+  }
   if (in_bf16) {
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
     return mse ? launch46_mode<uint16_t, true>(xb, amax, mode, amax_is_input, D, M, K, packed, scales, st)

@@ -92,7 +92,8 @@ def test_amax(shape, bf16, residual):
     assert_bitwise(to_np(nv.amax(to_dev(x), rd, "row")), oracle.amax(x, r0, mode="row"))
 
 
-@pytest.mark.parametrize("shape", [(1, 16), (128, 128), (304, 304), (128, 320), (64, 1024), (33, 7168)])
+@pytest.mark.parametrize("shape", [(1, 16), (128, 128), (304, 304), (128, 320), (64, 1024), (33, 7168),
+                                   (5, 12288), (3, 16384), (2, 16400)])
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("err_mode", ["mae", "mse"])
 @pytest.mark.parametrize("bound", [256, 448])

@@ -11,12 +11,15 @@
 // (S_enc * (1/6)), bound 448).
 //
 // Layout and mapping: blocks never straddle rows (K % 16 == 0), so the
-// [M, K] tensor is a flat run of M*K/16 blocks and block b owns codes
-// bytes [8b, 8b+8), scale byte b and elements [16b, 16b+16).  One lane owns
-// one block: it reads 32 B (bf16) or 64 B (fp32) with 128-bit loads, reduces
-// the block amax in registers, and writes 8 B of codes with one 64-bit store,
-// so a wave covers 64 consecutive blocks and every access of a wave is one
-// contiguous span.  The work is pure streaming (HBM-bound): no LDS, no MFMA.
+// [M, K] tensor is a flat run of M*K/16 blocks.  Four consecutive lanes own
+// one block, four elements each, so every load and store instruction of a
+// wave touches one contiguous span (bf16 8 B, fp32 16 B, residual 16 B, codes
+// 2 B per lane).  The block amax is reduced across the four lanes with two
+// DPP quad permutations.  Round-to-nearest codes come from the hardware
+// fp32 -> e2m1 conversion and the dequantized values from the exact e2m1 ->
+// fp32 conversion; blocks holding a NaN or an infinity, and stochastic
+// rounding, use the software encoder.  The work is HBM streaming: no LDS, no
+// MFMA.
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
@@ -24,13 +27,41 @@ namespace nvfp4 {
 
 constexpr int kThreads = 256;
 
+// Max over the four lanes of a quad (every lane of the quad gets it).
+NV_DEV uint32_t quad_max_u32(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);
+  return o > v ? o : v;
+}
+
+NV_DEV float quad_fmax(float v) {
+  v = fmaxf(v, bits2f((uint32_t)__builtin_amdgcn_update_dpp((int)f2bits(v), (int)f2bits(v), 0xB1, 0xF, 0xF, false)));
+  return fmaxf(v, bits2f((uint32_t)__builtin_amdgcn_update_dpp((int)f2bits(v), (int)f2bits(v), 0x4E, 0xF, 0xF, false)));
+}
+
+NV_DEV void load4(const uint16_t* p, float x[4]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  x[0] = bits2f(w.x << 16);
+  x[1] = bits2f(w.x & 0xFFFF0000u);
+  x[2] = bits2f(w.y << 16);
+  x[3] = bits2f(w.y & 0xFFFF0000u);
+}
+
+NV_DEV void load4(const float* p, float x[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+
 template <typename InT, bool HAS_RES, bool SR, bool GLOBAL, int OUT, bool CODES>
 __global__ __launch_bounds__(kThreads) void k_quant1x16(
     const InT* x, float* __restrict__ residual, const float* __restrict__ global_amax,
-    uint32_t key, int64_t nblk, uint8_t* __restrict__ packed, uint8_t* __restrict__ scales,
+    uint32_t key, int64_t ngroups, uint8_t* __restrict__ packed, uint8_t* __restrict__ scales,
     void* out) {
-  const int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (blk >= nblk) return;
+  // ngroups = M*K/4 is a multiple of 4, so a quad (one block) is either all
+  // in range or all out of range.
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= ngroups) return;
 
   float S_dec = 1.0f, mul = 0.0f;
   if (GLOBAL) {
@@ -39,131 +70,166 @@ __global__ __launch_bounds__(kThreads) void k_quant1x16(
     mul = S_enc * (1.0f / 6.0f);
   }
 
-  float xv[16];
-  load16(x + blk * 16, xv);
+  float xv[4];
+  load4(x + g * 4, xv);
+  float4 r4;
   if (HAS_RES) {
-    float r[16];
-    load16(residual + blk * 16, r);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) xv[i] = xv[i] + r[i];
+    r4 = *reinterpret_cast<const float4*>(residual + g * 4);
+    xv[0] = xv[0] + r4.x;
+    xv[1] = xv[1] + r4.y;
+    xv[2] = xv[2] + r4.z;
+    xv[3] = xv[3] + r4.w;
   }
-  float a = 0.0f;
+  // Block amax on the magnitude bit patterns (integer order = value order
+  // for non-NaN); a pattern >= 0x7F800000 flags a NaN or an infinity.
+  uint32_t ab = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xv[i]));
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = f2bits(xv[i]) & 0x7FFFFFFFu;
+    ab = m > ab ? m : ab;
+  }
+  ab = quad_max_u32(ab);
+  const bool special = ab >= 0x7F800000u;
+  float a;
+  if (!special) {
+    a = bits2f(ab);
+  } else {
+    a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a = fmaxf(a, fabsf(xv[i]));
+    a = quad_fmax(a);
+  }
 
-  float sigma = GLOBAL ? a * mul : a / 6.0f;
-  sigma = fminf(sigma, kE4m3Max);
-  const uint32_t sc = e4m3_encode(sigma);
+  float sigma = GLOBAL ? a * mul : div_guarded(a, 6.0f, 1.0f / 6.0f);
+  sigma = fminf(sigma, kE4m3Max);  // NaN -> 448
+  const uint32_t sc = hw_e4m3_pair(sigma, 0.0f) & 0xFFu;
   const float s = e4m3_decode(sc);
   const float rho = encode_reciprocal(s, S_dec);
 
-  uint32_t w[8];
-  if (SR) {
-    const uint32_t p0 = (uint32_t)(blk * 8);
+  uint32_t codes;
+  float xh[4];
+  if (!SR && !special) {
+    codes = hw_fp4_pair<0>(0u, xv[0] * rho, xv[1] * rho);
+    codes = hw_fp4_pair<1>(codes, xv[2] * rho, xv[3] * rho);
+    if (OUT != 0 || HAS_RES) {
+      const nv_f2 q01 = hw_fp4_values<0>(codes);
+      const nv_f2 q23 = hw_fp4_values<1>(codes);
+      xh[0] = (q01.x * s) * S_dec;
+      xh[1] = (q01.y * s) * S_dec;
+      xh[2] = (q23.x * s) * S_dec;
+      xh[3] = (q23.y * s) * S_dec;
+    }
+  } else {
+    uint32_t w0 = 0, w1 = 0;
+    if (SR) {
+      const uint32_t p0 = (uint32_t)(g * 2);
+      w0 = pcg_hash(p0 ^ key);
+      w1 = pcg_hash((p0 + 1u) ^ key);
+    }
+    codes = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w[j] = pcg_hash((p0 + j) ^ key);
-  }
-
-  uint32_t c0 = 0, c1 = 0;
-  float xh[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float v = fabsf(xv[i]) * rho;
-    float q;
-    uint32_t mag;
-    if (SR) mag = e2m1_sr(v, (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu, q);
-    else mag = e2m1_rtn(v, q);
-    const bool nan_v = (v != v);
-    const uint32_t neg = nan_v ? 0u : (f2bits(xv[i]) >> 31);
-    const uint32_t code = mag | (neg << 3);
-    if (i < 8) c0 |= code << (4 * i);
-    else c1 |= code << (4 * (i - 8));
-    const float val = neg ? -q : q;
-    xh[i] = (val * s) * S_dec;
+    for (int i = 0; i < 4; ++i) {
+      const float v = fabsf(xv[i]) * rho;
+      float q;
+      uint32_t mag;
+      if (SR) mag = e2m1_sr(v, ((i < 2 ? w0 : w1) >> ((i & 1) * 16)) & 0xFFFFu, q);
+      else mag = e2m1_rtn(v, q);
+      const bool nan_v = (v != v);
+      const uint32_t neg = nan_v ? 0u : (f2bits(xv[i]) >> 31);
+      codes |= (mag | (neg << 3)) << (4 * i);
+      const float val = neg ? -q : q;
+      xh[i] = (val * s) * S_dec;
+    }
   }
 
   if (CODES) {
-    reinterpret_cast<uint2*>(packed)[blk] = make_uint2(c0, c1);
-    scales[blk] = (uint8_t)sc;
+    reinterpret_cast<uint16_t*>(packed)[g] = (uint16_t)codes;
+    if ((threadIdx.x & 3) == 0) scales[g >> 2] = (uint8_t)sc;
   }
   if (HAS_RES) {
-    float r[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = xv[i] - xh[i];
-    store16(residual + blk * 16, r);
+    *reinterpret_cast<float4*>(residual + g * 4) =
+        make_float4(xv[0] - xh[0], xv[1] - xh[1], xv[2] - xh[2], xv[3] - xh[3]);
   }
-  if (OUT == 1) store16_bf16(reinterpret_cast<uint16_t*>(out) + blk * 16, xh);
-  if (OUT == 2) store16(reinterpret_cast<float*>(out) + blk * 16, xh);
+  if (OUT == 1) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + g * 4) =
+        make_uint2(f32_to_bf16(xh[0]) | (f32_to_bf16(xh[1]) << 16),
+                   f32_to_bf16(xh[2]) | (f32_to_bf16(xh[3]) << 16));
+  }
+  if (OUT == 2) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + g * 4) = make_float4(xh[0], xh[1], xh[2], xh[3]);
+  }
 }
 
 template <typename InT, bool HAS_RES, bool SR, bool GLOBAL>
-static int dispatch_out(const InT* x, float* res, const float* ga, uint32_t key, int64_t nblk,
+static int dispatch_out(const InT* x, float* res, const float* ga, uint32_t key, int64_t ng,
                         uint8_t* packed, uint8_t* scales, void* out, int out_kind,
                         hipStream_t st) {
-  const dim3 grid((unsigned)((nblk + kThreads - 1) / kThreads)), block(kThreads);
+  const dim3 grid((unsigned)((ng + kThreads - 1) / kThreads)), block(kThreads);
   const bool codes = packed != nullptr;
   if (out_kind == 0)
     hipLaunchKernelGGL((k_quant1x16<InT, HAS_RES, SR, GLOBAL, 0, true>), grid, block, 0, st,
-                       x, res, ga, key, nblk, packed, scales, out);
+                       x, res, ga, key, ng, packed, scales, out);
   else if (out_kind == 1 && codes)
     hipLaunchKernelGGL((k_quant1x16<InT, HAS_RES, SR, GLOBAL, 1, true>), grid, block, 0, st,
-                       x, res, ga, key, nblk, packed, scales, out);
+                       x, res, ga, key, ng, packed, scales, out);
   else if (out_kind == 1)
     hipLaunchKernelGGL((k_quant1x16<InT, HAS_RES, SR, GLOBAL, 1, false>), grid, block, 0, st,
-                       x, res, ga, key, nblk, packed, scales, out);
+                       x, res, ga, key, ng, packed, scales, out);
   else if (codes)
     hipLaunchKernelGGL((k_quant1x16<InT, HAS_RES, SR, GLOBAL, 2, true>), grid, block, 0, st,
-                       x, res, ga, key, nblk, packed, scales, out);
+                       x, res, ga, key, ng, packed, scales, out);
   else
     hipLaunchKernelGGL((k_quant1x16<InT, HAS_RES, SR, GLOBAL, 2, false>), grid, block, 0, st,
-                       x, res, ga, key, nblk, packed, scales, out);
+                       x, res, ga, key, ng, packed, scales, out);
   return (int)hipGetLastError();
 }
 
 template <typename InT, bool HAS_RES, bool SR>
 static int dispatch_global(const InT* x, float* res, const float* ga, uint32_t key,
-                           int64_t nblk, uint8_t* packed, uint8_t* scales, void* out,
+                           int64_t ng, uint8_t* packed, uint8_t* scales, void* out,
                            int out_kind, hipStream_t st) {
-  if (ga) return dispatch_out<InT, HAS_RES, SR, true>(x, res, ga, key, nblk, packed, scales, out, out_kind, st);
-  return dispatch_out<InT, HAS_RES, SR, false>(x, res, ga, key, nblk, packed, scales, out, out_kind, st);
+  if (ga) return dispatch_out<InT, HAS_RES, SR, true>(x, res, ga, key, ng, packed, scales, out, out_kind, st);
+  return dispatch_out<InT, HAS_RES, SR, false>(x, res, ga, key, ng, packed, scales, out, out_kind, st);
 }
 
 template <typename InT>
 static int dispatch_in(const InT* x, float* res, const float* ga, int sr, uint32_t key,
-                       int64_t nblk, uint8_t* packed, uint8_t* scales, void* out, int out_kind,
+                       int64_t ng, uint8_t* packed, uint8_t* scales, void* out, int out_kind,
                        hipStream_t st) {
-  if (res && sr) return dispatch_global<InT, true, true>(x, res, ga, key, nblk, packed, scales, out, out_kind, st);
-  if (res) return dispatch_global<InT, true, false>(x, res, ga, key, nblk, packed, scales, out, out_kind, st);
-  if (sr) return dispatch_global<InT, false, true>(x, res, ga, key, nblk, packed, scales, out, out_kind, st);
-  return dispatch_global<InT, false, false>(x, res, ga, key, nblk, packed, scales, out, out_kind, st);
+  if (res && sr) return dispatch_global<InT, true, true>(x, res, ga, key, ng, packed, scales, out, out_kind, st);
+  if (res) return dispatch_global<InT, true, false>(x, res, ga, key, ng, packed, scales, out, out_kind, st);
+  if (sr) return dispatch_global<InT, false, true>(x, res, ga, key, ng, packed, scales, out, out_kind, st);
+  return dispatch_global<InT, false, false>(x, res, ga, key, ng, packed, scales, out, out_kind, st);
 }
 
 int launch_quant1x16(const void* x, int in_bf16, int64_t M, int64_t K, float* residual,
                      const float* global_amax, int sr, uint32_t seed, uint32_t step,
                      uint8_t* packed, uint8_t* scales, void* out, int out_kind, void* stream) {
-  const int64_t nblk = M * K / 16;
-  if (nblk == 0) return 0;
+  const int64_t ng = M * K / 4;
+  if (ng == 0) return 0;
   const uint32_t key = rng_key_host(seed, step);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (in_bf16)
-    return dispatch_in(reinterpret_cast<const uint16_t*>(x), residual, global_amax, sr, key, nblk,
+    return dispatch_in(reinterpret_cast<const uint16_t*>(x), residual, global_amax, sr, key, ng,
                        packed, scales, out, out_kind, st);
-  return dispatch_in(reinterpret_cast<const float*>(x), residual, global_amax, sr, key, nblk,
+  return dispatch_in(reinterpret_cast<const float*>(x), residual, global_amax, sr, key, ng,
                      packed, scales, out, out_kind, st);
 }
 
 // ------------------------------------------------------------- dequantize
 
-// fp4-train, API: dequantize(packed, scale, M, K) -> bf16.  One lane per
-// 16-element block: x_hat = (val * s) * S_dec.
+// fp4-train, API: dequantize(packed, scale, M, K) -> bf16.  Four lanes per
+// 16-element block (2 code bytes each): x_hat = (val * s) * S_dec, with the
+// exact e2m1 -> fp32 hardware conversion for val.
 template <int SMODE, bool TILE16, bool BF16OUT>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ packed,
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ global_amax,
-                                                      float D, int64_t nbk, int64_t nblk,
+                                                      float D, int64_t nbk, int64_t ngroups,
                                                       void* __restrict__ out) {
-  const int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (blk >= nblk) return;
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= ngroups) return;
+  const int64_t blk = g >> 2;
   int64_t m = 0, b = blk;
   if (SMODE == 2 || TILE16) { m = blk / nbk; b = blk - m * nbk; }
   const int64_t sidx = TILE16 ? (m >> 4) * nbk + b : blk;
@@ -171,45 +237,42 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
   float S_dec = 1.0f;
   if (SMODE == 1) S_dec = global_amax[0] / D;
   if (SMODE == 2) S_dec = global_amax[m] / D;
-  const uint2 c = reinterpret_cast<const uint2*>(packed)[blk];
-  float xh[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t code = ((i < 8 ? c.x : c.y) >> (4 * (i & 7))) & 0xFu;
-    const uint32_t mag = code & 7u;
-    const float q = mag <= 4u ? (float)mag * 0.5f : (mag == 5u ? 3.0f : (mag == 6u ? 4.0f : 6.0f));
-    const float val = (code & 8u) ? -q : q;
-    xh[i] = (val * s) * S_dec;
-  }
-  if (BF16OUT) store16_bf16(reinterpret_cast<uint16_t*>(out) + blk * 16, xh);
-  else store16(reinterpret_cast<float*>(out) + blk * 16, xh);
+  const uint32_t c = reinterpret_cast<const uint16_t*>(packed)[g];
+  const nv_f2 q01 = hw_fp4_values<0>(c);
+  const nv_f2 q23 = hw_fp4_values<1>(c);
+  const float xh[4] = {(q01.x * s) * S_dec, (q01.y * s) * S_dec, (q23.x * s) * S_dec, (q23.y * s) * S_dec};
+  if (BF16OUT)
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + g * 4) =
+        make_uint2(f32_to_bf16(xh[0]) | (f32_to_bf16(xh[1]) << 16), f32_to_bf16(xh[2]) | (f32_to_bf16(xh[3]) << 16));
+  else
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + g * 4) = make_float4(xh[0], xh[1], xh[2], xh[3]);
 }
 
 template <int SMODE, bool TILE16>
 static int dq_out(const uint8_t* p, const uint8_t* s, const float* ga, float D, int64_t nbk,
-                  int64_t nblk, void* out, int out_bf16, hipStream_t st) {
-  const dim3 grid((unsigned)((nblk + kThreads - 1) / kThreads)), block(kThreads);
+                  int64_t ng, void* out, int out_bf16, hipStream_t st) {
+  const dim3 grid((unsigned)((ng + kThreads - 1) / kThreads)), block(kThreads);
   if (out_bf16)
-    hipLaunchKernelGGL((k_dequant<SMODE, TILE16, true>), grid, block, 0, st, p, s, ga, D, nbk, nblk, out);
+    hipLaunchKernelGGL((k_dequant<SMODE, TILE16, true>), grid, block, 0, st, p, s, ga, D, nbk, ng, out);
   else
-    hipLaunchKernelGGL((k_dequant<SMODE, TILE16, false>), grid, block, 0, st, p, s, ga, D, nbk, nblk, out);
+    hipLaunchKernelGGL((k_dequant<SMODE, TILE16, false>), grid, block, 0, st, p, s, ga, D, nbk, ng, out);
   return (int)hipGetLastError();
 }
 
 int launch_dequant(const uint8_t* packed, const uint8_t* scales, int64_t M, int64_t K,
                    int tile16, const float* global_amax, int scale_mode, float bound,
                    void* out, int out_bf16, void* stream) {
-  const int64_t nbk = K / 16, nblk = M * nbk;
-  if (nblk == 0) return 0;
+  const int64_t nbk = K / 16, ng = M * K / 4;
+  if (ng == 0) return 0;
   const float D = 6.0f * bound;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (tile16) {
-    if (scale_mode == 1) return dq_out<1, true>(packed, scales, global_amax, D, nbk, nblk, out, out_bf16, st);
-    return dq_out<0, true>(packed, scales, global_amax, D, nbk, nblk, out, out_bf16, st);
+    if (scale_mode == 1) return dq_out<1, true>(packed, scales, global_amax, D, nbk, ng, out, out_bf16, st);
+    return dq_out<0, true>(packed, scales, global_amax, D, nbk, ng, out, out_bf16, st);
   }
-  if (scale_mode == 1) return dq_out<1, false>(packed, scales, global_amax, D, nbk, nblk, out, out_bf16, st);
-  if (scale_mode == 2) return dq_out<2, false>(packed, scales, global_amax, D, nbk, nblk, out, out_bf16, st);
-  return dq_out<0, false>(packed, scales, global_amax, D, nbk, nblk, out, out_bf16, st);
+  if (scale_mode == 1) return dq_out<1, false>(packed, scales, global_amax, D, nbk, ng, out, out_bf16, st);
+  if (scale_mode == 2) return dq_out<2, false>(packed, scales, global_amax, D, nbk, ng, out, out_bf16, st);
+  return dq_out<0, false>(packed, scales, global_amax, D, nbk, ng, out, out_bf16, st);
 }
 
 }  // namespace nvfp4

@@ -10,8 +10,11 @@
 // holds row r of tile t: 16 consecutive elements read with 128-bit loads, so
 // each wave reads 16 rows x 128 contiguous bytes.  The tile amax is reduced
 // across the 16 lanes of the tile with cross-lane max (all 16 lanes of a tile
-// sit in one 16-lane row of the wave).  The rowwise codes go out as one 8-byte
-// store per lane.  For the columnwise codes each lane stages its 16 codes as
+// sit in one 16-lane row of the wave; DPP, no LDS).  Round-to-nearest codes
+// come from the hardware fp32 -> e2m1 conversion (exact for finite inputs;
+// tiles holding a NaN or an infinity and stochastic rounding use the
+// software encoder) and the scale byte from the exact fp32 -> e4m3
+// conversion.  The rowwise codes go out as one 8-byte store per lane.  For the columnwise codes each lane stages its 16 codes as
 // bytes in LDS; lane (t, c) then gathers column c of its tile and stores the
 // 16 codes of that column (8 bytes) into row k of packed_col.
 #include "nvfp4_device.hpp"
@@ -20,6 +23,19 @@
 namespace nvfp4 {
 
 constexpr int k2dThreads = 256;
+
+// Max over the 16 lanes of a DPP row (every lane of the row gets it): two
+// quad permutations, then the half-row and row mirrors.
+NV_DEV uint32_t row16_max_u32(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false);
+  return o > v ? o : v;
+}
 
 template <typename InT, bool SR, bool GLOBAL, bool COL>
 __global__ __launch_bounds__(k2dThreads) void k_quant2d(
@@ -42,51 +58,79 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
   }
 
   float xv[16];
-  float a = 0.0f;
+  uint32_t ab = 0;  // magnitude bit patterns: integer max = value max; >= 0x7F800000 flags NaN/inf
   if (active) {
     load16(x + row * K + col0, xv);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xv[i]));
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t m = f2bits(xv[i]) & 0x7FFFFFFFu;
+      ab = m > ab ? m : ab;
+    }
   }
+  ab = row16_max_u32(ab);
+  const bool special = ab >= 0x7F800000u;
+  float a = bits2f(ab);
+  if (special) {  // NaN-dropping tile amax (all 16 lanes of the tile take this branch)
+    float l = 0.0f;
+    if (active) {
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+      for (int i = 0; i < 16; ++i) l = fmaxf(l, fabsf(xv[i]));
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) l = fmaxf(l, __shfl_xor(l, off, 64));
+    a = l;
+  }
 
-  uint32_t codes[16];
+  uint32_t c0 = 0, c1 = 0;
   if (active) {
-    float sigma = GLOBAL ? a * mul : a / 6.0f;
+    float sigma = GLOBAL ? a * mul : div_guarded(a, 6.0f, 1.0f / 6.0f);
     sigma = fminf(sigma, kE4m3Max);
-    const uint32_t sc = e4m3_encode(sigma);
+    const uint32_t sc = hw_e4m3_pair(sigma, 0.0f) & 0xFFu;
     const float s = e4m3_decode(sc);
     const float rho = encode_reciprocal(s, S_dec);
-    uint32_t w[8];
-    if (SR) {
-      const uint32_t p0 = (uint32_t)((row * K + col0) >> 1);
+    if (!SR && !special) {
+      c0 = hw_fp4_pair<0>(c0, xv[0] * rho, xv[1] * rho);
+      c0 = hw_fp4_pair<1>(c0, xv[2] * rho, xv[3] * rho);
+      c0 = hw_fp4_pair<2>(c0, xv[4] * rho, xv[5] * rho);
+      c0 = hw_fp4_pair<3>(c0, xv[6] * rho, xv[7] * rho);
+      c1 = hw_fp4_pair<0>(c1, xv[8] * rho, xv[9] * rho);
+      c1 = hw_fp4_pair<1>(c1, xv[10] * rho, xv[11] * rho);
+      c1 = hw_fp4_pair<2>(c1, xv[12] * rho, xv[13] * rho);
+      c1 = hw_fp4_pair<3>(c1, xv[14] * rho, xv[15] * rho);
+    } else {
+      uint32_t w[8];
+      if (SR) {
+        const uint32_t p0 = (uint32_t)((row * K + col0) >> 1);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) w[j] = pcg_hash((p0 + j) ^ key);
-    }
-    uint32_t c0 = 0, c1 = 0;
+        for (int j = 0; j < 8; ++j) w[j] = pcg_hash((p0 + j) ^ key);
+      }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float v = fabsf(xv[i]) * rho;
-      float q;
-      uint32_t mag;
-      if (SR) mag = e2m1_sr(v, (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu, q);
-      else mag = e2m1_rtn(v, q);
-      const uint32_t neg = (v != v) ? 0u : (f2bits(xv[i]) >> 31);
-      codes[i] = mag | (neg << 3);
-      if (i < 8) c0 |= codes[i] << (4 * i);
-      else c1 |= codes[i] << (4 * (i - 8));
+      for (int i = 0; i < 16; ++i) {
+        const float v = fabsf(xv[i]) * rho;
+        float q;
+        uint32_t mag;
+        if (SR) mag = e2m1_sr(v, (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu, q);
+        else mag = e2m1_rtn(v, q);
+        const uint32_t neg = (v != v) ? 0u : (f2bits(xv[i]) >> 31);
+        const uint32_t code = mag | (neg << 3);
+        if (i < 8) c0 |= code << (4 * i);
+        else c1 |= code << (4 * (i - 8));
+      }
     }
     *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c0, c1);
     if (r == 0) tile_scales[(row0 / 16) * (K / 16) + col0 / 16] = (uint8_t)sc;
   }
   if (COL) {
+    // Stage the 16 codes of this tile row as bytes (one code per byte), then
+    // lane (t, c) gathers column c of its tile: 16 codes, rows 0..15, packed
+    // two per byte in row order into 8 bytes of packed_col row (col0 + c).
     if (active) {
-      uint32_t b[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = codes[4 * j] | (codes[4 * j + 1] << 8) | (codes[4 * j + 2] << 16) | (codes[4 * j + 3] << 24);
-      stage[threadIdx.x] = make_uint4(b[0], b[1], b[2], b[3]);
+      const uint32_t lo = c0, hi = c1;
+      stage[threadIdx.x] = make_uint4(
+          (lo & 0xFu) | ((lo >> 4) & 0xFu) << 8 | ((lo >> 8) & 0xFu) << 16 | ((lo >> 12) & 0xFu) << 24,
+          ((lo >> 16) & 0xFu) | ((lo >> 20) & 0xFu) << 8 | ((lo >> 24) & 0xFu) << 16 | ((lo >> 28) & 0xFu) << 24,
+          (hi & 0xFu) | ((hi >> 4) & 0xFu) << 8 | ((hi >> 8) & 0xFu) << 16 | ((hi >> 12) & 0xFu) << 24,
+          ((hi >> 16) & 0xFu) | ((hi >> 20) & 0xFu) << 8 | ((hi >> 24) & 0xFu) << 16 | ((hi >> 28) & 0xFu) << 24);
     }
     __syncthreads();
     if (active) {

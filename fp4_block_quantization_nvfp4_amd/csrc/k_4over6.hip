@@ -137,18 +137,6 @@ __global__ __launch_bounds__(k46MaxThreads) void k_4over6(const InT* __restrict_
 
 typedef unsigned short nv_us2 __attribute__((ext_vector_type(2)));
 
-NV_DEV float div_fast(float n, float D, float rD) {
-  const float q0 = n * rD;
-  const float rem = __builtin_fmaf(-q0, D, n);
-  return __builtin_fmaf(rem, rD, q0);
-}
-
-NV_DEV float div_guarded(float n, float D, float rD) {
-  const uint32_t e = (f2bits(n) >> 23) & 0xFFu;
-  if (e >= 10u && e <= 254u) return div_fast(n, D, rD);
-  return n / D;
-}
-
 // Max of the 16 bf16 magnitudes of a block as 16-bit patterns (for
 // non-NaN values the integer order is the value order; a NaN compares above
 // every finite value and infinity).
@@ -209,34 +197,40 @@ NV_DEV uint32_t wave_max_pk_u16(uint32_t v) {
   return pk_max_u16(pk_max_u16(r0, r1), pk_max_u16(r2, r3));
 }
 
-// Error sum of one candidate over a block, in element order: t points at the
-// candidate's row of the d table, c[2] holds its 16 codes; element i's d is
-// entry (code & 7).
+// Error sums of both candidates over a block, each in element order: t6 / t4
+// point at the candidates' rows of the d table, c6 / c4 hold their 16 codes;
+// element i's d is entry (code & 7).  The codes are first spread to one byte
+// per element (4 * (code & 7); even elements from the low nibbles, odd from
+// the high nibbles) so that each LDS address is one add with a byte-select
+// operand; the empty asm keeps the compiler from re-deriving per-element
+// shifts.  All 32 lookups are issued before the sums so the LDS latency of
+// one block overlaps.
 template <bool MSE>
-NV_DEV float error_sum(const float xv[16], const float* t, const uint32_t c[2]) {
-  const char* tb = reinterpret_cast<const char*>(t);
-  float E = 0.0f;
+NV_DEV void error_sums(const float xv[16], const float* t6, const uint32_t c6[2], const float* t4,
+                       const uint32_t c4[2], float& E6, float& E4) {
+  const char* tb6 = reinterpret_cast<const char*>(t6);
+  const char* tb4 = reinterpret_cast<const char*>(t4);
+  float d6[16], d4[16];
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    // 4 * (code & 7) of the even / odd elements, one byte each.  The empty
-    // asm keeps the compiler from re-deriving per-element shifts, so each
-    // lookup is one add with a byte-select operand.
-    uint32_t ev = (c[w] << 2) & 0x1C1C1C1Cu;
-    uint32_t od = (c[w] >> 2) & 0x1C1C1C1Cu;
-    asm("" : "+v"(ev), "+v"(od));
+    uint32_t ev6 = (c6[w] << 2) & 0x1C1C1C1Cu, od6 = (c6[w] >> 2) & 0x1C1C1C1Cu;
+    uint32_t ev4 = (c4[w] << 2) & 0x1C1C1C1Cu, od4 = (c4[w] >> 2) & 0x1C1C1C1Cu;
+    asm("" : "+v"(ev6), "+v"(od6), "+v"(ev4), "+v"(od4));
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float d0 = *reinterpret_cast<const float*>(tb + ((ev >> (8 * b)) & 0xFFu));
-      const float d1 = *reinterpret_cast<const float*>(tb + ((od >> (8 * b)) & 0xFFu));
-      const float u0 = fabsf(xv[8 * w + 2 * b]) - d0;
-      const float u1 = fabsf(xv[8 * w + 2 * b + 1]) - d1;
-      const float e0 = MSE ? u0 * u0 : fabsf(u0);
-      const float e1 = MSE ? u1 * u1 : fabsf(u1);
-      E = (w == 0 && b == 0) ? e0 : E + e0;
-      E = E + e1;
+      d6[8 * w + 2 * b] = *reinterpret_cast<const float*>(tb6 + ((ev6 >> (8 * b)) & 0xFFu));
+      d6[8 * w + 2 * b + 1] = *reinterpret_cast<const float*>(tb6 + ((od6 >> (8 * b)) & 0xFFu));
+      d4[8 * w + 2 * b] = *reinterpret_cast<const float*>(tb4 + ((ev4 >> (8 * b)) & 0xFFu));
+      d4[8 * w + 2 * b + 1] = *reinterpret_cast<const float*>(tb4 + ((od4 >> (8 * b)) & 0xFFu));
     }
   }
-  return E;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float u6 = fabsf(xv[i]) - d6[i], u4 = fabsf(xv[i]) - d4[i];
+    const float e6 = MSE ? u6 * u6 : fabsf(u6), e4 = MSE ? u4 * u4 : fabsf(u4);
+    E6 = (i == 0) ? e6 : E6 + e6;
+    E4 = (i == 0) ? e4 : E4 + e4;
+  }
 }
 
 template <int SEL>
@@ -387,8 +381,8 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
       uint32_t c6[2], c4[2];
       encode16_hw(xv, rhoT[k6], c6);
       encode16_hw(xv, rhoT[k4], c4);
-      const float E6 = error_sum<MSE>(xv, dT + k6 * kDStride, c6);
-      const float E4 = error_sum<MSE>(xv, dT + k4 * kDStride, c4);
+      float E6, E4;
+      error_sums<MSE>(xv, dT + k6 * kDStride, c6, dT + k4 * kDStride, c4, E6, E4);
       const bool pick4 = E4 < E6;
       out = pick4 ? make_uint2(c4[0], c4[1]) : make_uint2(c6[0], c6[1]);
       sbyte = pick4 ? k4 : k6;

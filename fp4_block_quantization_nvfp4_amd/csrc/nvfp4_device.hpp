@@ -140,6 +140,49 @@ NV_DEV void store16_bf16(uint16_t* p, const float x[16]) {
   q[1] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
+// ------------------------------------------------------------ divisions
+// n / D by reciprocal multiply plus one exact FMA remainder correction.
+// For D in {6, 1536, 2688} this equals the correctly rounded quotient for
+// every float32 numerator of magnitude >= 2^-117 (exponent field 10..254);
+// the host test suite proves it by exhausting all float32 numerators.
+NV_DEV float div_fast(float n, float D, float rD) {
+  const float q0 = n * rD;
+  const float rem = __builtin_fmaf(-q0, D, n);
+  return __builtin_fmaf(rem, rD, q0);
+}
+
+// Correctly rounded n / D: the fast sequence where it is proven exact, the
+// true division elsewhere (tiny, zero, infinite or NaN numerators).
+NV_DEV float div_guarded(float n, float D, float rD) {
+  const uint32_t e = (f2bits(n) >> 23) & 0xFFu;
+  if (e >= 10u && e <= 254u) return div_fast(n, D, rD);
+  return n / D;
+}
+
+// ------------------------------------------------- hardware conversions
+// gfx950 fp32 -> e2m1 (two values, round-to-nearest-even, saturating at
+// +-6; scale operand 1.0 means no scaling) into byte SEL of c.  Equal to the
+// software encoder for every finite and infinite input; a negative NaN gives
+// 0xF instead of 0x7, so callers keep NaN inputs off this path.
+template <int SEL>
+NV_DEV uint32_t hw_fp4_pair(uint32_t c, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, a, b, 1.0f, SEL);
+}
+
+typedef float nv_f2 __attribute__((ext_vector_type(2)));
+
+// e2m1 byte SEL of c -> the two exact values (low nibble first).
+template <int SEL>
+NV_DEV nv_f2 hw_fp4_values(uint32_t c) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, SEL);
+}
+
+// gfx950 fp32 -> e4m3 of two scales in [0, 448] (bytes 0 and 1): equal to
+// e4m3_encode on every float32 in that range (checked exhaustively).
+NV_DEV uint32_t hw_e4m3_pair(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
 // Global scale from amax A and D = 6 * bound: S_enc = min(D / A, FLT_MAX),
 // S_dec = A / D (true divisions).
 NV_DEV void global_scales(float A, float D, float& S_enc, float& S_dec) {

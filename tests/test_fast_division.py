@@ -24,7 +24,7 @@ def checker(tmp_path_factory):
     return exe
 
 
-@pytest.mark.parametrize("D,mode", [(6.0, "bf16"), (1536.0, "f32"), (2688.0, "f32")])
+@pytest.mark.parametrize("D,mode", [(6.0, "bf16"), (6.0, "f32"), (1536.0, "f32"), (2688.0, "f32")])
 def test_fast_division_is_correctly_rounded(checker, D, mode):
     args = [checker, repr(D)] + (["bf16"] if mode == "bf16" else [])
     res = subprocess.run(args, capture_output=True, text=True, timeout=600)

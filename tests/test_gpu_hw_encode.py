@@ -1,0 +1,72 @@
+"""Dense checks of the hardware-assisted encode paths against the oracle.
+
+The round-to-nearest kernels take element codes from the gfx950 fp32 -> e2m1
+conversion and scale bytes from the fp32 -> e4m3 conversion.  Here the
+ordinary quantize entry point is driven so that those conversions see dense
+sweeps of their inputs, and every code and scale byte is compared with the
+CPU oracle:
+
+* element codes: blocks [6, v_1 .. v_15] have amax 6, scale 1.0 and encode
+  reciprocal 1, so each v is rounded as it stands; the v sweep every float32
+  in [0, 8) whose low 6 mantissa bits are zero, +-2^12 ulps around every
+  rounding midpoint, and both signs;
+* scale bytes: one block per amax value, over every positive finite bf16
+  value up to 2688 (sigma = a / 6 up to 448) and 2^20 float32 values.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp4_block_quantization_nvfp4_amd as nv
+from tests.gpu_util import assert_bitwise, need_gpu, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _unit_scale_blocks(v):
+    n = (len(v) + 14) // 15
+    vv = np.zeros(n * 15, np.float32)
+    vv[: len(v)] = v
+    x = np.empty((n, 16), np.float32)
+    x[:, 0] = 6.0
+    x[:, 1:] = vv.reshape(n, 15)
+    return x.reshape(-1, 64) if n % 4 == 0 else x
+
+
+def test_e2m1_conversion_dense_sweep():
+    grid = np.arange(0, 0x41000000, 64, dtype=np.uint32).view(np.float32)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32).view(np.uint32)
+    near = (mids[:, None].astype(np.int64) + np.arange(-4096, 4097)[None, :]).reshape(-1).astype(np.uint32)
+    v = np.concatenate([grid, near.view(np.float32)])
+    v = np.concatenate([v, -v, np.array([7.0, 1e30, -1e30, np.inf, -np.inf, 0.0, -0.0], np.float32)])
+    for chunk in np.array_split(v, 4):
+        x = _unit_scale_blocks(chunk)
+        M, K = x.shape
+        wp, ws = oracle.quantize(x)
+        p, s = nv.quantize(to_dev(x))
+        assert_bitwise(to_np(s), ws, "scales")
+        assert_bitwise(to_np(p), wp, "codes")
+
+
+def test_e4m3_scale_dense_sweep():
+    b = np.arange(1, 0x7F80, dtype=np.uint32)
+    a_bf16 = (b << 16).view(np.float32)
+    a_bf16 = a_bf16[a_bf16 <= 2688.0]
+    rng = np.random.default_rng(0)
+    a_f32 = (2.0 ** rng.uniform(-20, np.log2(3000.0), 1 << 20)).astype(np.float32)
+    for a in (a_bf16, a_f32):
+        x = np.zeros((len(a), 16), np.float32)
+        x[:, 0] = a
+        x[:, 1] = -a * np.float32(0.5)
+        for dt in ("f32", "bf16"):
+            xin = x if dt == "f32" else oracle.f32_to_bf16_bits(x)
+            wp, ws = oracle.quantize(xin)
+            p, s = nv.quantize(to_dev(xin))
+            assert_bitwise(to_np(s), ws, f"scales {dt}")
+            assert_bitwise(to_np(p), wp, f"codes {dt}")

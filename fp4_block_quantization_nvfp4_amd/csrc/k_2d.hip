@@ -5,8 +5,9 @@
 // one pass (the fused row + column kernel the four-over-six pull request lists
 // as a follow-up), so no caller-side transpose is needed.
 //
-// Mapping: a workgroup of 256 lanes covers a 16-row x 256-column strip, i.e.
-// 16 tiles side by side, four per wave.  Lane (t, r) = (tid / 16, tid % 16)
+// Mapping: a workgroup of 256 lanes covers 256 columns and walks down up to
+// 16 strips of 16 rows (a 256 x 256 region); in each strip it holds 16 tiles
+// side by side, four per wave.  Lane (t, r) = (tid / 16, tid % 16)
 // holds row r of tile t: 16 consecutive elements read with 128-bit loads, so
 // each wave reads 16 rows x 128 contiguous bytes.  The tile amax is reduced
 // across the 16 lanes of the tile with cross-lane max (all 16 lanes of a tile
@@ -37,18 +38,22 @@ NV_DEV uint32_t row16_max_u32(uint32_t v) {
   return o > v ? o : v;
 }
 
+constexpr int kStrips = 16;         // 16-row strips per workgroup (256 rows)
+constexpr int kColStride = kStrips + 1;  // uint2 per column in the column buffer (+1 spreads banks)
+
 template <typename InT, bool SR, bool GLOBAL, bool COL>
 __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     const InT* __restrict__ x, const float* __restrict__ global_amax, uint32_t key, int64_t M,
     int64_t K, uint8_t* __restrict__ packed_row, uint8_t* __restrict__ packed_col,
     uint8_t* __restrict__ tile_scales, int64_t ncolg) {
-  __shared__ uint4 stage[k2dThreads];
+  __shared__ uint4 stage[16 * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (bank spread)
+  __shared__ uint2 colbuf[COL ? 256 * kColStride : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
-  const int64_t strip = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - strip * ncolg;
+  const int64_t sg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - sg * ncolg;
   const int64_t col0 = cg * 256 + 16 * t;
-  const int64_t row0 = strip * 16;
-  const int64_t row = row0 + r;
   const bool active = col0 < K;  // uniform over the 16 lanes of a tile
+  const int64_t nstrips_total = M / 16;
+  const int nst = (int)((nstrips_total - sg * kStrips) < kStrips ? (nstrips_total - sg * kStrips) : kStrips);
 
   float S_dec = 1.0f, mul = 0.0f;
   if (GLOBAL) {
@@ -57,93 +62,147 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     mul = S_enc * (1.0f / 6.0f);
   }
 
-  float xv[16];
-  uint32_t ab = 0;  // magnitude bit patterns: integer max = value max; >= 0x7F800000 flags NaN/inf
+  // The next strip's 16 elements are loaded while the current one is
+  // encoded (two register buffers of raw input).
+  constexpr int kRaw = sizeof(InT) * 16 / 16;  // uint4 per 16 elements
+  uint4 nxt[kRaw];
   if (active) {
-    load16(x + row * K + col0, xv);
+    const uint4* p = reinterpret_cast<const uint4*>(x + (sg * kStrips * 16 + r) * K + col0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t m = f2bits(xv[i]) & 0x7FFFFFFFu;
-      ab = m > ab ? m : ab;
-    }
+    for (int i = 0; i < kRaw; ++i) nxt[i] = p[i];
   }
-  ab = row16_max_u32(ab);
-  const bool special = ab >= 0x7F800000u;
-  float a = bits2f(ab);
-  if (special) {  // NaN-dropping tile amax (all 16 lanes of the tile take this branch)
-    float l = 0.0f;
+  for (int st = 0; st < nst; ++st) {
+    const int64_t row0 = (sg * kStrips + st) * 16;
+    const int64_t row = row0 + r;
+    uint4 cur[kRaw];
+#pragma unroll
+    for (int i = 0; i < kRaw; ++i) cur[i] = nxt[i];
+    if (active && st + 1 < nst) {
+      const uint4* p = reinterpret_cast<const uint4*>(x + (row + 16) * K + col0);
+#pragma unroll
+      for (int i = 0; i < kRaw; ++i) nxt[i] = p[i];
+    }
+    float xv[16];
+    uint32_t ab = 0;  // magnitude bit patterns: integer max = value max; >= 0x7F800000 flags NaN/inf
     if (active) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) l = fmaxf(l, fabsf(xv[i]));
-    }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) l = fmaxf(l, __shfl_xor(l, off, 64));
-    a = l;
-  }
-
-  uint32_t c0 = 0, c1 = 0;
-  if (active) {
-    float sigma = GLOBAL ? a * mul : div_guarded(a, 6.0f, 1.0f / 6.0f);
-    sigma = fminf(sigma, kE4m3Max);
-    const uint32_t sc = hw_e4m3_pair(sigma, 0.0f) & 0xFFu;
-    const float s = e4m3_decode(sc);
-    const float rho = encode_reciprocal(s, S_dec);
-    if (!SR && !special) {
-      c0 = hw_fp4_pair<0>(c0, xv[0] * rho, xv[1] * rho);
-      c0 = hw_fp4_pair<1>(c0, xv[2] * rho, xv[3] * rho);
-      c0 = hw_fp4_pair<2>(c0, xv[4] * rho, xv[5] * rho);
-      c0 = hw_fp4_pair<3>(c0, xv[6] * rho, xv[7] * rho);
-      c1 = hw_fp4_pair<0>(c1, xv[8] * rho, xv[9] * rho);
-      c1 = hw_fp4_pair<1>(c1, xv[10] * rho, xv[11] * rho);
-      c1 = hw_fp4_pair<2>(c1, xv[12] * rho, xv[13] * rho);
-      c1 = hw_fp4_pair<3>(c1, xv[14] * rho, xv[15] * rho);
-    } else {
-      uint32_t w[8];
-      if (SR) {
-        const uint32_t p0 = (uint32_t)((row * K + col0) >> 1);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w[j] = pcg_hash((p0 + j) ^ key);
-      }
+      load16(reinterpret_cast<const InT*>(cur), xv);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float v = fabsf(xv[i]) * rho;
-        float q;
-        uint32_t mag;
-        if (SR) mag = e2m1_sr(v, (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu, q);
-        else mag = e2m1_rtn(v, q);
-        const uint32_t neg = (v != v) ? 0u : (f2bits(xv[i]) >> 31);
-        const uint32_t code = mag | (neg << 3);
-        if (i < 8) c0 |= code << (4 * i);
-        else c1 |= code << (4 * (i - 8));
+        const uint32_t m = f2bits(xv[i]) & 0x7FFFFFFFu;
+        ab = m > ab ? m : ab;
       }
     }
-    *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c0, c1);
-    if (r == 0) tile_scales[(row0 / 16) * (K / 16) + col0 / 16] = (uint8_t)sc;
+    ab = row16_max_u32(ab);
+    const bool special = ab >= 0x7F800000u;
+    float a = bits2f(ab);
+    if (special) {  // NaN-dropping tile amax (all 16 lanes of the tile take this branch)
+      float l = 0.0f;
+      if (active) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) l = fmaxf(l, fabsf(xv[i]));
+      }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) l = fmaxf(l, __shfl_xor(l, off, 64));
+      a = l;
+    }
+
+    uint32_t c0 = 0, c1 = 0;
+    if (active) {
+      float sigma = GLOBAL ? a * mul : div_guarded(a, 6.0f, 1.0f / 6.0f);
+      sigma = fminf(sigma, kE4m3Max);
+      const uint32_t sc = hw_e4m3_pair(sigma, 0.0f) & 0xFFu;
+      const float s = e4m3_decode(sc);
+      const float rho = encode_reciprocal(s, S_dec);
+      if (SR && !special) {
+        // stochastic rounding on the bit patterns, then the hardware
+        // conversion encodes the (on-grid, signed) results exactly
+        const uint32_t p0 = (uint32_t)((row * K + col0) >> 1);
+        float rv[16];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t w = pcg_hash((p0 + j) ^ key);
+          const float r0 = e2m1_sr_bits(fabsf(xv[2 * j]) * rho, (w << 7) & 0x7FFF80u);
+          const float r1 = e2m1_sr_bits(fabsf(xv[2 * j + 1]) * rho, (w >> 9) & 0x7FFF80u);
+          rv[2 * j] = bits2f(f2bits(r0) | (f2bits(xv[2 * j]) & 0x80000000u));
+          rv[2 * j + 1] = bits2f(f2bits(r1) | (f2bits(xv[2 * j + 1]) & 0x80000000u));
+        }
+        c0 = hw_fp4_pair<0>(c0, rv[0], rv[1]);
+        c0 = hw_fp4_pair<1>(c0, rv[2], rv[3]);
+        c0 = hw_fp4_pair<2>(c0, rv[4], rv[5]);
+        c0 = hw_fp4_pair<3>(c0, rv[6], rv[7]);
+        c1 = hw_fp4_pair<0>(c1, rv[8], rv[9]);
+        c1 = hw_fp4_pair<1>(c1, rv[10], rv[11]);
+        c1 = hw_fp4_pair<2>(c1, rv[12], rv[13]);
+        c1 = hw_fp4_pair<3>(c1, rv[14], rv[15]);
+      } else if (!SR && !special) {
+        c0 = hw_fp4_pair<0>(c0, xv[0] * rho, xv[1] * rho);
+        c0 = hw_fp4_pair<1>(c0, xv[2] * rho, xv[3] * rho);
+        c0 = hw_fp4_pair<2>(c0, xv[4] * rho, xv[5] * rho);
+        c0 = hw_fp4_pair<3>(c0, xv[6] * rho, xv[7] * rho);
+        c1 = hw_fp4_pair<0>(c1, xv[8] * rho, xv[9] * rho);
+        c1 = hw_fp4_pair<1>(c1, xv[10] * rho, xv[11] * rho);
+        c1 = hw_fp4_pair<2>(c1, xv[12] * rho, xv[13] * rho);
+        c1 = hw_fp4_pair<3>(c1, xv[14] * rho, xv[15] * rho);
+      } else {
+        uint32_t w[8];
+        if (SR) {
+          const uint32_t p0 = (uint32_t)((row * K + col0) >> 1);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = pcg_hash((p0 + j) ^ key);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float v = fabsf(xv[i]) * rho;
+          float q;
+          uint32_t mag;
+          if (SR) mag = e2m1_sr(v, (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu, q);
+          else mag = e2m1_rtn(v, q);
+          const uint32_t neg = (v != v) ? 0u : (f2bits(xv[i]) >> 31);
+          const uint32_t code = mag | (neg << 3);
+          if (i < 8) c0 |= code << (4 * i);
+          else c1 |= code << (4 * (i - 8));
+        }
+      }
+      *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c0, c1);
+      if (r == 0) tile_scales[(row0 / 16) * (K / 16) + col0 / 16] = (uint8_t)sc;
+    }
+    if (COL) {
+      // Stage the 16 codes of this tile row one per byte; lane (t, c) then
+      // gathers column c of its tile (rows 0..15, two codes per byte in row
+      // order) into the column buffer slot of this strip.
+      if (active) {
+        stage[17 * t + r] = make_uint4(
+            (c0 & 0xFu) | ((c0 >> 4) & 0xFu) << 8 | ((c0 >> 8) & 0xFu) << 16 | ((c0 >> 12) & 0xFu) << 24,
+            ((c0 >> 16) & 0xFu) | ((c0 >> 20) & 0xFu) << 8 | ((c0 >> 24) & 0xFu) << 16 | ((c0 >> 28) & 0xFu) << 24,
+            (c1 & 0xFu) | ((c1 >> 4) & 0xFu) << 8 | ((c1 >> 8) & 0xFu) << 16 | ((c1 >> 12) & 0xFu) << 24,
+            ((c1 >> 16) & 0xFu) | ((c1 >> 20) & 0xFu) << 8 | ((c1 >> 24) & 0xFu) << 16 | ((c1 >> 28) & 0xFu) << 24);
+      }
+      __syncthreads();
+      if (active) {
+        const uint8_t* tile = reinterpret_cast<const uint8_t*>(&stage[17 * t]);
+        const int c = r;
+        uint32_t o0 = 0, o1 = 0;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const uint32_t code = tile[16 * rr + c];
+          if (rr < 8) o0 |= code << (4 * rr);
+          else o1 |= code << (4 * (rr - 8));
+        }
+        colbuf[(16 * t + c) * kColStride + st] = make_uint2(o0, o1);
+      }
+      __syncthreads();
+    }
   }
   if (COL) {
-    // Stage the 16 codes of this tile row as bytes (one code per byte), then
-    // lane (t, c) gathers column c of its tile: 16 codes, rows 0..15, packed
-    // two per byte in row order into 8 bytes of packed_col row (col0 + c).
-    if (active) {
-      const uint32_t lo = c0, hi = c1;
-      stage[threadIdx.x] = make_uint4(
-          (lo & 0xFu) | ((lo >> 4) & 0xFu) << 8 | ((lo >> 8) & 0xFu) << 16 | ((lo >> 12) & 0xFu) << 24,
-          ((lo >> 16) & 0xFu) | ((lo >> 20) & 0xFu) << 8 | ((lo >> 24) & 0xFu) << 16 | ((lo >> 28) & 0xFu) << 24,
-          (hi & 0xFu) | ((hi >> 4) & 0xFu) << 8 | ((hi >> 8) & 0xFu) << 16 | ((hi >> 12) & 0xFu) << 24,
-          ((hi >> 16) & 0xFu) | ((hi >> 20) & 0xFu) << 8 | ((hi >> 24) & 0xFu) << 16 | ((hi >> 28) & 0xFu) << 24);
-    }
-    __syncthreads();
-    if (active) {
-      const uint8_t* tile = reinterpret_cast<const uint8_t*>(&stage[16 * t]);
-      const int c = r;  // this lane now handles column c of its tile
-      uint32_t o0 = 0, o1 = 0;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const uint32_t code = tile[16 * rr + c];
-        if (rr < 8) o0 |= code << (4 * rr);
-        else o1 |= code << (4 * (rr - 8));
-      }
-      *reinterpret_cast<uint2*>(packed_col + (col0 + c) * (M / 2) + row0 / 2) = make_uint2(o0, o1);
+    // Each column of this workgroup owns nst * 8 contiguous bytes of its
+    // packed_col row; 16 lanes write one column (8 bytes each), so every
+    // store instruction covers four whole column segments.
+    const int q = threadIdx.x & 15;
+    for (int cc = threadIdx.x >> 4; cc < 256; cc += k2dThreads / 16) {
+      const int64_t col = cg * 256 + cc;
+      if (col < K && q < nst)
+        *reinterpret_cast<uint2*>(packed_col + col * (M / 2) + sg * (kStrips * 8) + q * 8) =
+            colbuf[cc * kColStride + q];
     }
   }
 }
@@ -152,7 +211,8 @@ template <typename InT, bool SR, bool GLOBAL>
 static int launch2d_col(const InT* x, const float* ga, uint32_t key, int64_t M, int64_t K,
                         uint8_t* pr, uint8_t* pc, uint8_t* ts, hipStream_t st) {
   const int64_t ncolg = (K + 255) / 256;
-  const dim3 grid((unsigned)(ncolg * (M / 16))), block(k2dThreads);
+  const int64_t nsg = (M / 16 + kStrips - 1) / kStrips;
+  const dim3 grid((unsigned)(ncolg * nsg)), block(k2dThreads);
   if (pc) hipLaunchKernelGGL((k_quant2d<InT, SR, GLOBAL, true>), grid, block, 0, st, x, ga, key, M, K, pr, pc, ts, ncolg);
   else hipLaunchKernelGGL((k_quant2d<InT, SR, GLOBAL, false>), grid, block, 0, st, x, ga, key, M, K, pr, pc, ts, ncolg);
   return (int)hipGetLastError();

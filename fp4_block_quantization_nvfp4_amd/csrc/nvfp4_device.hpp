@@ -80,6 +80,26 @@ NV_DEV uint32_t e2m1_sr(float v, uint32_t u16, float& q) {
   return (uint32_t)n + off;
 }
 
+// The same stochastic rounding on the bit pattern of v (finite, >= 0),
+// returning the rounded magnitude as a float.  u7 = u16 << 7.  With
+// vm = min(v, 6): on [1, 6] the grid keeps one mantissa bit, so the
+// fraction is the low 22 mantissa bits and u < f  <=>  u16 * 2^6 < frac22;
+// on [0.5, 1) it keeps none and u < f  <=>  u16 * 2^7 < frac23; below 0.5
+// the grid step is 0.5 and u < 2v  <=>  u16 * 2^-17 < v.  lo = the bits with
+// the fraction cleared, hi = lo plus one unit of the kept bit (a carry into
+// the exponent gives the next binade).  Equal to e2m1_sr's value.
+NV_DEV float e2m1_sr_bits(float v, uint32_t u7) {
+  const float vm = fminf(v, 6.0f);
+  const uint32_t b = f2bits(vm);
+  const uint32_t ge1 = b >= 0x3F800000u ? 1u : 0u;
+  const uint32_t mask = 0x7FFFFFu >> ge1;
+  const uint32_t frac = b & mask;
+  const uint32_t lo = b - frac;
+  uint32_t r = (u7 < (frac << ge1)) ? lo + mask + 1u : lo;
+  if (b < 0x3F000000u) r = ((float)u7 * 0x1p-24f < vm) ? 0x3F000000u : 0u;
+  return bits2f(r);
+}
+
 // fp32 -> bf16 bits, round-to-nearest-even; NaN -> 0x7FC0.
 NV_DEV uint32_t f32_to_bf16(float f) {
   uint32_t u = f2bits(f);

@@ -42,6 +42,7 @@ from .formats import (  # noqa: F401
     e2m1_sr_index,
     e4m3_decode,
     e4m3_encode,
+    e4m3_encode_up,
     f32_to_bf16_bits,
 )
 from .rng import pcg_hash, rng_key, sr_u16  # noqa: F401
@@ -52,5 +53,7 @@ from .nvfp4 import (  # noqa: F401
     quantize,
     quantize_2d,
     quantize_4over6,
+    quantize_4over6_2d,
+    quantize_rowcol,
     unpack_codes,
 )

@@ -79,6 +79,22 @@ def e4m3_encode(sigma) -> np.ndarray:
     return _nearest_even_index(sigma, E4M3_VALUES).astype(np.uint8)
 
 
+def e4m3_encode_up(sigma) -> np.ndarray:
+    """fp32 scale sigma (>= 0, not NaN) -> the smallest e4m3 value >= sigma
+    (round toward +inf), saturating to 0x7E (448) when sigma exceeds it.
+
+    This is the "truncation-free" scale of the transposition-invariant 2D
+    paper (abstract: "truncation-free scaling"): with s >= block_amax / 6 the
+    largest element maps to at most 6, so no element is clipped.  The page
+    gives no formula; rounding the scale up is the plainest reading.
+    """
+    sigma = np.asarray(sigma, dtype=np.float32)
+    if np.isnan(sigma).any() or (np.signbit(sigma) & (sigma != 0)).any():
+        raise ValueError("e4m3_encode_up expects non-negative, non-NaN scales")
+    idx = np.searchsorted(E4M3_VALUES.astype(np.float64), sigma.astype(np.float64), side="left")
+    return np.minimum(idx, len(E4M3_VALUES) - 1).astype(np.uint8)
+
+
 def e2m1_rtn_index(v) -> np.ndarray:
     """Magnitude v (>= 0, not NaN) -> e2m1 magnitude index by RNE on the
     grid, saturating at 6 (index 7).  NaN handling is the caller's."""

@@ -27,6 +27,7 @@ from .formats import (
     e2m1_sr_index,
     e4m3_decode,
     e4m3_encode,
+    e4m3_encode_up,
     f32_to_bf16_bits,
 )
 from .rng import sr_u16
@@ -338,7 +339,50 @@ def quantize_4over6(x, global_amax, err_mode="mae", bound=256.0, block="1x16"):
     return pack_codes(codes), sbyte
 
 
-def quantize_2d(x, stochastic=False, seed=0, step=0, global_amax=None, row_offset=0):
+def quantize_4over6_2d(x, global_amax, err_mode="mae", bound=256.0):
+    """Four-over-six on transposition-invariant 16x16 tiles (per-tensor
+    global amax) -> (packed_row [M, K/2], packed_col [K, M/2], tile_scales
+    [M/16, K/16]).  The tile's candidate choice uses the 16 per-row
+    sequential errors combined by the exact width-16 tree (four-over-six
+    pull request, CuTe DSL kernel Design); rowwise and columnwise outputs are
+    the same codes, so they share the tile scale (transposition-invariant 2D
+    paper, abstract)."""
+    packed, scales = quantize_4over6(x, global_amax, err_mode=err_mode, bound=bound, block="16x16")
+    xp = _to_f32(x)
+    M, K = xp.shape
+    codes = unpack_codes(packed).reshape(M, K)
+    return packed, pack_codes(codes.T), scales
+
+
+def quantize_rowcol(x, global_amax, four_over_six=False, err_mode="mae", bound=448.0):
+    """Rowwise and columnwise 1x16 quantization of the same tensor in one
+    call -> (packed_row [M, K/2], scales_row [M, K/16], packed_col [K, M/2],
+    scales_col [K, M/16]).  The columnwise outputs are the rowwise
+    quantization of X^T (blocks of 16 consecutive rows of one column), as the
+    backward-pass operands need (four-over-six pull request, What: backward
+    against saved columnwise codes; Follow-up fusions: a fused row + col
+    kernel instead of x.t().contiguous()).  Round-to-nearest with one
+    per-tensor global amax: the standard path (sigma = a * (S_enc * (1/6)),
+    bound 448) or four-over-six (bound 256 or 448)."""
+    xp = _to_f32(x)
+    M, K = xp.shape
+    if M % 16:
+        raise ValueError("columnwise 1x16 blocks need M % 16 == 0")
+    A = np.float32(global_amax)
+    xt = np.ascontiguousarray(xp.T)
+    if four_over_six:
+        pr, sr = quantize_4over6(xp, A, err_mode=err_mode, bound=bound)
+        pc, scol = quantize_4over6(xt, A, err_mode=err_mode, bound=bound)
+    else:
+        if bound != 448.0:
+            raise ValueError("the standard path uses bound 448")
+        pr, sr = quantize(xp, global_amax=A)
+        pc, scol = quantize(xt, global_amax=A)
+    return pr, sr, pc, scol
+
+
+def quantize_2d(x, stochastic=False, seed=0, step=0, global_amax=None, row_offset=0,
+                truncation_free=False):
     """Transposition-invariant 2D NVFP4: one e4m3 scale per 16x16 tile,
     shared by X and X^T ("Stable FP4 Training via Transposition-Invariant
     Block Quantization", abstract), optionally with stochastic rounding.
@@ -365,7 +409,7 @@ def quantize_2d(x, stochastic=False, seed=0, step=0, global_amax=None, row_offse
         with np.errstate(invalid="ignore", over="ignore"):
             sigma = a * (S_enc * (F32(1.0) / F32(6.0)))
     sigma = np.fmin(sigma, E4M3_MAX).astype(np.float32)
-    sbyte = e4m3_encode(sigma)
+    sbyte = e4m3_encode_up(sigma) if truncation_free else e4m3_encode(sigma)
     s = e4m3_decode(sbyte)
     rho = _encode_reciprocal(s, S_dec)
     rho_el = np.repeat(np.repeat(rho, 16, axis=0), 16, axis=1)

@@ -270,7 +270,7 @@ def extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle, steps, war
     lib.nvfp4_amax(wd[0].data_ptr(), L.BF16, Mt, Kt, None, L.SCALE_TENSOR, ga.data_ptr(), wsb.data_ptr(), wsz, stream)
     ms_amax = time_ms(torch, lambda i: lib.nvfp4_amax(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, None, L.SCALE_TENSOR,
                                                        ga.data_ptr(), wsb.data_ptr(), wsz, stream), warmup, steps)
-    ms_2d = time_ms(torch, lambda i: lib.nvfp4_quantize_2d(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(), 1, 0, 0,
+    ms_2d = time_ms(torch, lambda i: lib.nvfp4_quantize_2d(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(), 1, 0, 0, 0,
                                                             pr[i % 2].data_ptr(), pc[i % 2].data_ptr(),
                                                             ts[i % 2].data_ptr(), stream), warmup, steps)
     A = oracle.amax(wb)

@@ -11,5 +11,7 @@ from .api import (  # noqa: F401
     qdq,
     quantize,
     quantize_2d,
+    quantize_4over6_2d,
+    quantize_rowcol,
     quantize_4over6,
 )

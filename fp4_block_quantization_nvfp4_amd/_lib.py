@@ -29,7 +29,9 @@ SIGNATURES = {
     "nvfp4_dequantize": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _i32, _f32, _vp, _i32, _vp]),
     "nvfp4_qdq": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _u32, _u32, _vp, _i32, _vp, _vp, _vp]),
     "nvfp4_quantize_4over6": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _i32, _f32, _vp, _vp, _vp]),
-    "nvfp4_quantize_2d": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _u32, _u32, _vp, _vp, _vp, _vp]),
+    "nvfp4_quantize_2d": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _u32, _u32, _i32, _vp, _vp, _vp, _vp]),
+    "nvfp4_quantize_rowcol": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp]),
+    "nvfp4_quantize_4over6_2d": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _vp, _vp]),
 }
 
 

@@ -175,9 +175,11 @@ def quantize_4over6(x, global_amax=None, *, err_mode="mae", e4m3_scale_bound=256
     return packed, scale, global_amax
 
 
-def quantize_2d(x, global_amax=None, stochastic=False, seed=0, step=0, columnwise=True):
+def quantize_2d(x, global_amax=None, stochastic=False, seed=0, step=0, columnwise=True,
+                truncation_free=False):
     """Transposition-invariant 16x16 quantize -> (packed_row [M, K/2],
-    packed_col [K, M/2] or None, tile_scales [M/16, K/16])."""
+    packed_col [K, M/2] or None, tile_scales [M/16, K/16]).  truncation_free
+    rounds each tile scale up instead of to nearest."""
     M, K = _check_input(x, "quantize_2d")
     ga = _resolve_global(global_amax, x)
     packed_row = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
@@ -185,9 +187,52 @@ def quantize_2d(x, global_amax=None, stochastic=False, seed=0, step=0, columnwis
     tiles = torch.empty((M // 16, K // 16), dtype=torch.uint8, device=x.device)
     L.check(L.lib().nvfp4_quantize_2d(_ptr(x), _DT[x.dtype], M, K, _ptr(ga),
                                       L.SR if stochastic else L.RTN, seed & 0xFFFFFFFF,
-                                      step & 0xFFFFFFFF, _ptr(packed_row), _ptr(packed_col),
-                                      _ptr(tiles), _stream()), "nvfp4_quantize_2d")
+                                      step & 0xFFFFFFFF, int(bool(truncation_free)),
+                                      _ptr(packed_row), _ptr(packed_col), _ptr(tiles), _stream()),
+            "nvfp4_quantize_2d")
     return packed_row, packed_col, tiles
+
+
+def quantize_rowcol(x, global_amax="compute", *, four_over_six=False, err_mode="mae",
+                    e4m3_scale_bound=None):
+    """Rowwise and columnwise 1x16 NVFP4 of x in one pass (RTN, one global
+    amax) -> (packed_row [M, K/2], scales_row [M, K/16], packed_col [K, M/2],
+    scales_col [K, M/16]); the columnwise pair is the quantization of x^T.
+    Standard encode (bound 448) or four-over-six (bound 256 by default)."""
+    M, K = _check_input(x, "quantize_rowcol")
+    ga = _resolve_global(global_amax, x)
+    if ga is None:
+        raise ValueError("quantize_rowcol needs a global amax ('compute', a float or a tensor)")
+    bound = e4m3_scale_bound if e4m3_scale_bound is not None else (256 if four_over_six else 448)
+    err = {"mae": L.MAE, "mse": L.MSE}[err_mode]
+    dev = x.device
+    pr = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sr = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    pc = torch.empty((K, M // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((K, M // 16), dtype=torch.uint8, device=dev)
+    L.check(L.lib().nvfp4_quantize_rowcol(_ptr(x), _DT[x.dtype], M, K, _ptr(ga), int(bool(four_over_six)),
+                                          err, float(bound), _ptr(pr), _ptr(sr), _ptr(pc), _ptr(sc),
+                                          _stream()), "nvfp4_quantize_rowcol")
+    return pr, sr, pc, sc
+
+
+def quantize_4over6_2d(x, global_amax="compute", *, err_mode="mae", e4m3_scale_bound=256,
+                       columnwise=True):
+    """Four-over-six on 16x16 tiles (one global amax) -> (packed_row [M, K/2],
+    packed_col [K, M/2] or None, tile_scales [M/16, K/16])."""
+    M, K = _check_input(x, "quantize_4over6_2d")
+    ga = _resolve_global(global_amax, x)
+    if ga is None:
+        raise ValueError("quantize_4over6_2d needs a global amax ('compute', a float or a tensor)")
+    err = {"mae": L.MAE, "mse": L.MSE}[err_mode]
+    dev = x.device
+    pr = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    pc = torch.empty((K, M // 2), dtype=torch.uint8, device=dev) if columnwise else None
+    ts = torch.empty((M // 16, K // 16), dtype=torch.uint8, device=dev)
+    L.check(L.lib().nvfp4_quantize_4over6_2d(_ptr(x), _DT[x.dtype], M, K, _ptr(ga), err,
+                                             float(e4m3_scale_bound), _ptr(pr), _ptr(pc), _ptr(ts),
+                                             _stream()), "nvfp4_quantize_4over6_2d")
+    return pr, pc, ts
 
 
 class ErrorFeedback:

@@ -145,19 +145,58 @@ nvfp4_status nvfp4_quantize_4over6(const void* x, nvfp4_dtype dt, int64_t M, int
 
 nvfp4_status nvfp4_quantize_2d(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
                                const float* global_amax, nvfp4_round rnd, uint32_t seed,
-                               uint32_t step, uint8_t* packed_row, uint8_t* packed_col,
-                               uint8_t* tile_scales, void* stream) {
+                               uint32_t step, int truncation_free, uint8_t* packed_row,
+                               uint8_t* packed_col, uint8_t* tile_scales, void* stream) {
   if (nvfp4_status st = check_shape(M, K, true)) return st;
   if (!dtype_ok(dt)) return NVFP4_E_DTYPE;
   if (rnd != NVFP4_RTN && rnd != NVFP4_SR) return NVFP4_E_ARG;
+  if (truncation_free != 0 && truncation_free != 1) return NVFP4_E_ARG;
   if (M == 0 || K == 0) return NVFP4_OK;
   if (!x || !packed_row || !tile_scales) return NVFP4_E_NULL;
   if (!aligned(x, 16) || !aligned(packed_row, 8) || !aligned(packed_col, 8) ||
       !aligned(global_amax, 4))
     return NVFP4_E_ALIGN;
   return hip_status(nvfp4::launch_quant2d(x, dt == NVFP4_BF16, M, K, global_amax,
-                                          rnd == NVFP4_SR, seed, step, packed_row, packed_col,
-                                          tile_scales, stream));
+                                          rnd == NVFP4_SR, seed, step, truncation_free,
+                                          packed_row, packed_col, tile_scales, stream));
+}
+
+nvfp4_status nvfp4_quantize_rowcol(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
+                                   const float* global_amax, int four_over_six, nvfp4_err err,
+                                   float bound, uint8_t* packed_row, uint8_t* scales_row,
+                                   uint8_t* packed_col, uint8_t* scales_col, void* stream) {
+  if (nvfp4_status st = check_shape(M, K, true)) return st;
+  if (!dtype_ok(dt)) return NVFP4_E_DTYPE;
+  if (four_over_six != 0 && four_over_six != 1) return NVFP4_E_ARG;
+  if (err != NVFP4_MAE && err != NVFP4_MSE) return NVFP4_E_ARG;
+  if (four_over_six ? !(bound == 256.0f || bound == 448.0f) : bound != 448.0f) return NVFP4_E_ARG;
+  if (M == 0 || K == 0) return NVFP4_OK;
+  if (!x || !global_amax || !packed_row || !scales_row || !packed_col || !scales_col)
+    return NVFP4_E_NULL;
+  if (!aligned(x, 16) || !aligned(packed_row, 8) || !aligned(packed_col, 8) ||
+      !aligned(global_amax, 4))
+    return NVFP4_E_ALIGN;
+  return hip_status(nvfp4::launch_rowcol(x, dt == NVFP4_BF16, M, K, global_amax, four_over_six,
+                                         err == NVFP4_MSE, bound, packed_row, scales_row,
+                                         packed_col, scales_col, stream));
+}
+
+nvfp4_status nvfp4_quantize_4over6_2d(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
+                                      const float* global_amax, nvfp4_err err, float bound,
+                                      uint8_t* packed_row, uint8_t* packed_col,
+                                      uint8_t* tile_scales, void* stream) {
+  if (nvfp4_status st = check_shape(M, K, true)) return st;
+  if (!dtype_ok(dt)) return NVFP4_E_DTYPE;
+  if (err != NVFP4_MAE && err != NVFP4_MSE) return NVFP4_E_ARG;
+  if (!(bound == 256.0f || bound == 448.0f)) return NVFP4_E_ARG;
+  if (M == 0 || K == 0) return NVFP4_OK;
+  if (!x || !global_amax || !packed_row || !tile_scales) return NVFP4_E_NULL;
+  if (!aligned(x, 16) || !aligned(packed_row, 8) || !aligned(packed_col, 8) ||
+      !aligned(global_amax, 4))
+    return NVFP4_E_ALIGN;
+  return hip_status(nvfp4::launch_4over6_2d(x, dt == NVFP4_BF16, M, K, global_amax,
+                                            err == NVFP4_MSE, bound, packed_row, packed_col,
+                                            tile_scales, stream));
 }
 
 }  // extern "C"

@@ -41,7 +41,7 @@ NV_DEV uint32_t row16_max_u32(uint32_t v) {
 constexpr int kStrips = 16;         // 16-row strips per workgroup (256 rows)
 constexpr int kColStride = kStrips + 1;  // uint2 per column in the column buffer (+1 spreads banks)
 
-template <typename InT, bool SR, bool GLOBAL, bool COL>
+template <typename InT, bool SR, bool GLOBAL, bool COL, bool UP>
 __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     const InT* __restrict__ x, const float* __restrict__ global_amax, uint32_t key, int64_t M,
     int64_t K, uint8_t* __restrict__ packed_row, uint8_t* __restrict__ packed_col,
@@ -110,8 +110,12 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     if (active) {
       float sigma = GLOBAL ? a * mul : div_guarded(a, 6.0f, 1.0f / 6.0f);
       sigma = fminf(sigma, kE4m3Max);
-      const uint32_t sc = hw_e4m3_pair(sigma, 0.0f) & 0xFFu;
-      const float s = e4m3_decode(sc);
+      uint32_t sc = hw_e4m3_pair(sigma, 0.0f) & 0xFFu;
+      float s = e4m3_decode(sc);
+      if (UP && s < sigma && sc < 0x7Eu) {  // truncation-free: smallest e4m3 value >= sigma
+        sc += 1u;
+        s = e4m3_decode(sc);
+      }
       const float rho = encode_reciprocal(s, S_dec);
       if (SR && !special) {
         // stochastic rounding on the bit patterns, then the hardware
@@ -207,37 +211,45 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
   }
 }
 
-template <typename InT, bool SR, bool GLOBAL>
+template <typename InT, bool SR, bool GLOBAL, bool UP>
 static int launch2d_col(const InT* x, const float* ga, uint32_t key, int64_t M, int64_t K,
                         uint8_t* pr, uint8_t* pc, uint8_t* ts, hipStream_t st) {
   const int64_t ncolg = (K + 255) / 256;
   const int64_t nsg = (M / 16 + kStrips - 1) / kStrips;
   const dim3 grid((unsigned)(ncolg * nsg)), block(k2dThreads);
-  if (pc) hipLaunchKernelGGL((k_quant2d<InT, SR, GLOBAL, true>), grid, block, 0, st, x, ga, key, M, K, pr, pc, ts, ncolg);
-  else hipLaunchKernelGGL((k_quant2d<InT, SR, GLOBAL, false>), grid, block, 0, st, x, ga, key, M, K, pr, pc, ts, ncolg);
+  if (pc) hipLaunchKernelGGL((k_quant2d<InT, SR, GLOBAL, true, UP>), grid, block, 0, st, x, ga, key, M, K, pr, pc, ts, ncolg);
+  else hipLaunchKernelGGL((k_quant2d<InT, SR, GLOBAL, false, UP>), grid, block, 0, st, x, ga, key, M, K, pr, pc, ts, ncolg);
   return (int)hipGetLastError();
 }
 
-template <typename InT>
+template <typename InT, bool UP>
 static int launch2d_typed(const InT* x, const float* ga, int sr, uint32_t key, int64_t M,
                           int64_t K, uint8_t* pr, uint8_t* pc, uint8_t* ts, hipStream_t st) {
-  if (sr && ga) return launch2d_col<InT, true, true>(x, ga, key, M, K, pr, pc, ts, st);
-  if (sr) return launch2d_col<InT, true, false>(x, ga, key, M, K, pr, pc, ts, st);
-  if (ga) return launch2d_col<InT, false, true>(x, ga, key, M, K, pr, pc, ts, st);
-  return launch2d_col<InT, false, false>(x, ga, key, M, K, pr, pc, ts, st);
+  if (sr && ga) return launch2d_col<InT, true, true, UP>(x, ga, key, M, K, pr, pc, ts, st);
+  if (sr) return launch2d_col<InT, true, false, UP>(x, ga, key, M, K, pr, pc, ts, st);
+  if (ga) return launch2d_col<InT, false, true, UP>(x, ga, key, M, K, pr, pc, ts, st);
+  return launch2d_col<InT, false, false, UP>(x, ga, key, M, K, pr, pc, ts, st);
+}
+
+template <typename InT>
+static int launch2d_round(const InT* x, const float* ga, int sr, uint32_t key, int round_up,
+                          int64_t M, int64_t K, uint8_t* pr, uint8_t* pc, uint8_t* ts,
+                          hipStream_t st) {
+  if (round_up) return launch2d_typed<InT, true>(x, ga, sr, key, M, K, pr, pc, ts, st);
+  return launch2d_typed<InT, false>(x, ga, sr, key, M, K, pr, pc, ts, st);
 }
 
 int launch_quant2d(const void* x, int in_bf16, int64_t M, int64_t K, const float* global_amax,
-                   int sr, uint32_t seed, uint32_t step, uint8_t* packed_row,
+                   int sr, uint32_t seed, uint32_t step, int round_up, uint8_t* packed_row,
                    uint8_t* packed_col, uint8_t* tile_scales, void* stream) {
   if (M == 0 || K == 0) return 0;
   const uint32_t key = rng_key_host(seed, step);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (in_bf16)
-    return launch2d_typed(reinterpret_cast<const uint16_t*>(x), global_amax, sr, key, M, K,
-                          packed_row, packed_col, tile_scales, st);
-  return launch2d_typed(reinterpret_cast<const float*>(x), global_amax, sr, key, M, K, packed_row,
-                        packed_col, tile_scales, st);
+    return launch2d_round(reinterpret_cast<const uint16_t*>(x), global_amax, sr, key, round_up, M,
+                          K, packed_row, packed_col, tile_scales, st);
+  return launch2d_round(reinterpret_cast<const float*>(x), global_amax, sr, key, round_up, M, K,
+                        packed_row, packed_col, tile_scales, st);
 }
 
 }  // namespace nvfp4

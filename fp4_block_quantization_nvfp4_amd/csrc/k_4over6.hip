@@ -18,6 +18,7 @@
 // is HBM streaming plus per-element VALU arithmetic; no LDS beyond the
 // workgroup reduction and no MFMA.
 #include "nvfp4_device.hpp"
+#include "nvfp4_fos.hpp"
 #include "nvfp4_launch.hpp"
 
 namespace nvfp4 {
@@ -37,33 +38,6 @@ NV_DEV float block_absmax16(const InT* p, float xv[16]) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xv[i]));
   return a;
-}
-
-// One candidate: codes (two u32 of packed nibbles) and the error sum.
-template <bool MSE>
-NV_DEV float candidate(const float xv[16], float s, float rho, float A, float D, uint32_t& c0,
-                       uint32_t& c1) {
-  float E = 0.0f;
-  c0 = 0;
-  c1 = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float ax = fabsf(xv[i]);
-    const float v = ax * rho;
-    float q;
-    const uint32_t mag = e2m1_rtn(v, q);
-    const uint32_t neg = (v != v) ? 0u : (f2bits(xv[i]) >> 31);
-    const uint32_t code = mag | (neg << 3);
-    if (i < 8) c0 |= code << (4 * i);
-    else c1 |= code << (4 * (i - 8));
-    // |x - d| and (x - d)^2 are unchanged when both signs are flipped, so
-    // the error is taken on magnitudes.
-    const float d = ((q * s) * A) / D;
-    const float t = ax - d;
-    const float e = MSE ? t * t : fabsf(t);
-    E = (i == 0) ? e : E + e;
-  }
-  return E;
 }
 
 template <typename InT, bool MSE, int MODE>
@@ -169,13 +143,6 @@ NV_DEV void unpack16(const uint4 r0, const uint4 r1, float xv[16]) {
   }
 }
 
-NV_DEV float e2m1_value(uint32_t m) {
-  return m <= 4u ? (float)m * 0.5f : (m == 5u ? 3.0f : (m == 6u ? 4.0f : 6.0f));
-}
-
-constexpr int kDStride = 9;  // floats per scale code in the d table (8 used; 9 spreads LDS banks)
-constexpr int kTabFloats = 128 + 127 * kDStride;  // rho[128] then d[127][kDStride]
-
 // Lane-wise max of two packed pairs of u16.
 NV_DEV uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(nv_us2, a),
@@ -195,62 +162,6 @@ NV_DEV uint32_t wave_max_pk_u16(uint32_t v) {
   const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
   const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
   return pk_max_u16(pk_max_u16(r0, r1), pk_max_u16(r2, r3));
-}
-
-// Error sums of both candidates over a block, each in element order: t6 / t4
-// point at the candidates' rows of the d table, c6 / c4 hold their 16 codes;
-// element i's d is entry (code & 7).  The codes are first spread to one byte
-// per element (4 * (code & 7); even elements from the low nibbles, odd from
-// the high nibbles) so that each LDS address is one add with a byte-select
-// operand; the empty asm keeps the compiler from re-deriving per-element
-// shifts.  All 32 lookups are issued before the sums so the LDS latency of
-// one block overlaps.
-template <bool MSE>
-NV_DEV void error_sums(const float xv[16], const float* t6, const uint32_t c6[2], const float* t4,
-                       const uint32_t c4[2], float& E6, float& E4) {
-  const char* tb6 = reinterpret_cast<const char*>(t6);
-  const char* tb4 = reinterpret_cast<const char*>(t4);
-  float d6[16], d4[16];
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    uint32_t ev6 = (c6[w] << 2) & 0x1C1C1C1Cu, od6 = (c6[w] >> 2) & 0x1C1C1C1Cu;
-    uint32_t ev4 = (c4[w] << 2) & 0x1C1C1C1Cu, od4 = (c4[w] >> 2) & 0x1C1C1C1Cu;
-    asm("" : "+v"(ev6), "+v"(od6), "+v"(ev4), "+v"(od4));
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      d6[8 * w + 2 * b] = *reinterpret_cast<const float*>(tb6 + ((ev6 >> (8 * b)) & 0xFFu));
-      d6[8 * w + 2 * b + 1] = *reinterpret_cast<const float*>(tb6 + ((od6 >> (8 * b)) & 0xFFu));
-      d4[8 * w + 2 * b] = *reinterpret_cast<const float*>(tb4 + ((ev4 >> (8 * b)) & 0xFFu));
-      d4[8 * w + 2 * b + 1] = *reinterpret_cast<const float*>(tb4 + ((od4 >> (8 * b)) & 0xFFu));
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float u6 = fabsf(xv[i]) - d6[i], u4 = fabsf(xv[i]) - d4[i];
-    const float e6 = MSE ? u6 * u6 : fabsf(u6), e4 = MSE ? u4 * u4 : fabsf(u4);
-    E6 = (i == 0) ? e6 : E6 + e6;
-    E4 = (i == 0) ? e4 : E4 + e4;
-  }
-}
-
-template <int SEL>
-NV_DEV void cvt_pair(uint32_t& c, float a, float b) {
-  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, a, b, 1.0f, SEL);
-}
-
-// Codes of one candidate: v = x * rho, rounded to e2m1 by the hardware
-// conversion, two elements per instruction, even element in the low nibble.
-NV_DEV void encode16_hw(const float xv[16], float rho, uint32_t c[2]) {
-  c[0] = 0u;
-  c[1] = 0u;
-  cvt_pair<0>(c[0], xv[0] * rho, xv[1] * rho);
-  cvt_pair<1>(c[0], xv[2] * rho, xv[3] * rho);
-  cvt_pair<2>(c[0], xv[4] * rho, xv[5] * rho);
-  cvt_pair<3>(c[0], xv[6] * rho, xv[7] * rho);
-  cvt_pair<0>(c[1], xv[8] * rho, xv[9] * rho);
-  cvt_pair<1>(c[1], xv[10] * rho, xv[11] * rho);
-  cvt_pair<2>(c[1], xv[12] * rho, xv[13] * rho);
-  cvt_pair<3>(c[1], xv[14] * rho, xv[15] * rho);
 }
 
 // A block takes the table-free software path when it holds a NaN or an
@@ -328,8 +239,9 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
     const float a = bits2f(info[j] << 16);
     const float sig6r = div_fast(a, 6.0f, 1.0f / 6.0f) * S_enc;
     const float sig4r = sig6r * 1.5f;
-    const uint32_t kk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(sig6r, kE4m3Max),
-                                                                  fminf(sig4r, kE4m3Max), 0, false);
+    // (masked to 7 bits: only a negative given amax, which is invalid input,
+    // could set the sign bit; the mask keeps table indexes in range)
+    const uint32_t kk = hw_e4m3_pair(fminf(sig6r, kE4m3Max), fminf(sig4r, kE4m3Max)) & 0x7F7Fu;
     const bool fast = (tid + kRowThreads * j < nbk) && !slow_block(info[j]);
     if (fast) span = pk_max_u16(span, ((0xFFu - (kk & 0xFFu)) << 16) | ((kk >> 8) & 0xFFu));
     info[j] |= kk << 16;
@@ -340,17 +252,7 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
   const uint32_t sp = pk_max_u16(red[1][0], red[1][1]);
   const int kmin = 0xFF - (int)(sp >> 16), kmax = (int)(sp & 0xFFFFu);
 
-  if (kmin <= kmax) {
-    const float rD = 1.0f / D;
-    for (int k = kmin + tid; k <= kmax; k += kRowThreads)
-      rhoT[k] = encode_reciprocal(e4m3_decode((uint32_t)k), S_dec);
-    const float qm = e2m1_value((uint32_t)(tid & 7));
-    const int n = (kmax - kmin + 1) * 8;
-    for (int e = tid; e < n; e += kRowThreads) {
-      const uint32_t k = (uint32_t)kmin + (uint32_t)(e >> 3);
-      dT[k * kDStride + (e & 7)] = div_guarded((qm * e4m3_decode(k)) * A, D, rD);
-    }
-  }
+  build_fos_tables(rhoT, dT, kmin, kmax, A, D, S_dec, tid, kRowThreads);
   __syncthreads();
 
 #pragma unroll

@@ -1,0 +1,383 @@
+// Two kernels that produce the forward (rowwise) and the transposed
+// (columnwise) NVFP4 operands of one tensor in a single pass over it, with
+// one per-tensor global amax and round-to-nearest:
+//
+//  * k_rowcol - 1x16 blocks along K for X and, independently, 1x16 blocks
+//    along M (16 consecutive rows of one column) for X^T, each block with its
+//    own scale: the standard encode (sigma = a * (S_enc * (1/6)), bound 448)
+//    or four-over-six (bound 256 or 448).  This is the fused row + column
+//    kernel that the four-over-six pull request lists among its follow-up
+//    fusions, replacing a caller-side transpose and second quantize for the
+//    backward operands.
+//  * k_4over6_2d - four-over-six on 16x16 tiles: one scale per tile, shared
+//    by X and X^T (transposition-invariant paper, abstract); each tile row
+//    sums its 16 errors in element order, the 16 row sums are combined by the
+//    exact width-16 tree of the pull request's CuTe DSL kernel Design, and
+//    map-to-4 is kept iff its tile error is strictly lower.
+//
+// Mapping (both): a workgroup of 256 lanes covers 256 columns and walks down
+// up to kStripsRC strips of 16 rows.  In a strip it holds 16 tiles side by
+// side, four per wave; lane (t, r) = (tid / 16, tid % 16) reads row r of tile
+// t (16 consecutive elements, 128-bit loads) and the next strip's row is
+// loaded while the current one is encoded.  Columnwise blocks are formed in
+// LDS: k_rowcol stages the tile's values (lane (t, c) then reads column c of
+// tile t), k_4over6_2d stages its codes (the same codes, transposed).  The
+// columnwise codes and scales of each column are gathered in LDS across the
+// strips and written out once per workgroup as whole column segments.
+//
+// Four-over-six: with A and D fixed for the tensor, the encode reciprocals
+// and dequant values of every scale code are tabulated in LDS once per
+// workgroup.  Blocks or tiles that hold a NaN or an infinity take the
+// software encoder and true divisions.
+#include "nvfp4_device.hpp"
+#include "nvfp4_fos.hpp"
+#include "nvfp4_launch.hpp"
+
+namespace nvfp4 {
+
+constexpr int kRcThreads = 256;
+constexpr int kStripsRC = 8;                  // 16-row strips per workgroup
+constexpr int kColStrideRC = kStripsRC + 1;   // per-column slots in the column buffers (+1: banks)
+constexpr int kXRow = 20;                     // floats per staged row (16 used; 80 B keeps 16 B alignment)
+constexpr int kXTile = 16 * kXRow + 16;       // floats per staged tile (+16 shifts tiles across banks)
+
+// Max over the 16 lanes of a DPP row (every lane of the row gets it).
+NV_DEV uint32_t row16_max(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false);
+  v = o > v ? o : v;
+  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false);
+  return o > v ? o : v;
+}
+
+// Sum of the 16 lanes' values of a tile in the tree order
+// ((g0+g8)+(g4+g12)) + ((g2+g10)+(g6+g14)) for the even lanes and the same
+// over the odd lanes, then even + odd: exchanging with lane ^ 8, ^ 4, ^ 2,
+// ^ 1 forms exactly these partial sums (fp addition is commutative, so both
+// partners of an exchange hold the same bits) and every lane ends with the
+// tile total.
+NV_DEV float tree16_sum(float e) {
+  e = e + __shfl_xor(e, 8, 64);
+  e = e + __shfl_xor(e, 4, 64);
+  e = e + __shfl_xor(e, 2, 64);
+  e = e + __shfl_xor(e, 1, 64);
+  return e;
+}
+
+NV_DEV uint32_t absmax_bits16(const float v[16]) {
+  uint32_t ab = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t m = f2bits(v[i]) & 0x7FFFFFFFu;
+    ab = m > ab ? m : ab;
+  }
+  return ab;
+}
+
+NV_DEV float absmax_nan_drop16(const float v[16]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+  return a;
+}
+
+// Standard 1x16 block with a global scale: sigma = a * mul, mul =
+// S_enc * (1/6); returns the scale byte, codes in c.
+NV_DEV uint32_t block_standard(const float v[16], float mul, float S_dec, uint32_t c[2]) {
+  const uint32_t ab = absmax_bits16(v);
+  if (ab < 0x7F800000u) {
+    const uint32_t sc = hw_e4m3_pair(fminf(bits2f(ab) * mul, kE4m3Max), 0.0f) & 0xFFu;
+    encode16_hw(v, encode_reciprocal(e4m3_decode(sc), S_dec), c);
+    return sc;
+  }
+  const uint32_t sc = e4m3_encode(fminf(absmax_nan_drop16(v) * mul, kE4m3Max));
+  encode16_sw(v, encode_reciprocal(e4m3_decode(sc), S_dec), c);
+  return sc;
+}
+
+// Four-over-six 1x16 block; returns the chosen scale byte, codes in c.
+template <bool MSE>
+NV_DEV uint32_t block_fos(const float v[16], float S_enc, float S_dec, float A, float D,
+                          const float* rhoT, const float* dT, uint32_t c[2]) {
+  const uint32_t ab = absmax_bits16(v);
+  if (ab < 0x7F800000u) {
+    const float sig6 = div_guarded(bits2f(ab), 6.0f, 1.0f / 6.0f) * S_enc;
+    // (the mask only matters for a negative amax, which is invalid input: it
+    // keeps the table index in range)
+    const uint32_t kk = hw_e4m3_pair(fminf(sig6, kE4m3Max), fminf(sig6 * 1.5f, kE4m3Max)) & 0x7F7Fu;
+    const uint32_t k6 = kk & 0xFFu, k4 = kk >> 8;
+    uint32_t c6[2], c4[2];
+    encode16_hw(v, rhoT[k6], c6);
+    encode16_hw(v, rhoT[k4], c4);
+    float E6, E4;
+    error_sums<MSE>(v, dT + k6 * kDStride, c6, dT + k4 * kDStride, c4, E6, E4);
+    const bool pick4 = E4 < E6;
+    c[0] = pick4 ? c4[0] : c6[0];
+    c[1] = pick4 ? c4[1] : c6[1];
+    return pick4 ? k4 : k6;
+  }
+  const float sig6 = (absmax_nan_drop16(v) / 6.0f) * S_enc;
+  const uint32_t k6 = e4m3_encode(fminf(sig6, kE4m3Max));
+  const uint32_t k4 = e4m3_encode(fminf(sig6 * 1.5f, kE4m3Max));
+  const float s6 = e4m3_decode(k6), s4 = e4m3_decode(k4);
+  uint32_t a0, a1, b0, b1;
+  const float E6 = candidate<MSE>(v, s6, encode_reciprocal(s6, S_dec), A, D, a0, a1);
+  const float E4 = candidate<MSE>(v, s4, encode_reciprocal(s4, S_dec), A, D, b0, b1);
+  const bool pick4 = E4 < E6;
+  c[0] = pick4 ? b0 : a0;
+  c[1] = pick4 ? b1 : a1;
+  return pick4 ? k4 : k6;
+}
+
+// Raw input of 16 elements (uint4 words) and its conversion to fp32.
+template <typename InT>
+struct Raw16 {
+  static constexpr int kWords = sizeof(InT);  // uint4 per 16 elements: 2 (bf16) or 4 (fp32)
+  uint4 w[kWords];
+  NV_DEV void load(const InT* p) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) w[i] = q[i];
+  }
+  NV_DEV void to_f32(float v[16]) const { load16(reinterpret_cast<const InT*>(w), v); }
+};
+
+// Write the column buffers of a workgroup: column cc of the workgroup owns
+// nst * 8 contiguous code bytes of its packed_col row (and nst scale bytes of
+// its scales_col row); 16 lanes serve one column.
+NV_DEV void flush_columns(const uint2* colbuf, const uint8_t* csbuf, int64_t cg, int64_t sg, int nst,
+                          int64_t M, int64_t K, uint8_t* packed_col, uint8_t* scales_col) {
+  const int q = threadIdx.x & 15;
+  for (int cc = threadIdx.x >> 4; cc < 256; cc += kRcThreads / 16) {
+    const int64_t col = cg * 256 + cc;
+    if (col < K && q < nst) {
+      const int64_t strip = sg * kStripsRC + q;
+      *reinterpret_cast<uint2*>(packed_col + col * (M / 2) + strip * 8) = colbuf[cc * kColStrideRC + q];
+      if (scales_col) scales_col[col * (M / 16) + strip] = csbuf[cc * kColStrideRC + q];
+    }
+  }
+}
+
+template <typename InT, bool FOS, bool MSE>
+__global__ __launch_bounds__(kRcThreads) void k_rowcol(
+    const InT* __restrict__ x, const float* __restrict__ global_amax, float D, int64_t M, int64_t K,
+    uint8_t* __restrict__ packed_row, uint8_t* __restrict__ scales_row,
+    uint8_t* __restrict__ packed_col, uint8_t* __restrict__ scales_col, int64_t ncolg) {
+  __shared__ __attribute__((aligned(16))) float xs[16 * kXTile];
+  __shared__ uint2 colbuf[256 * kColStrideRC];
+  __shared__ uint8_t csbuf[256 * kColStrideRC];
+  __shared__ __attribute__((aligned(16))) float tab[FOS ? kTabFloats : 1];
+  const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
+  const int64_t sg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - sg * ncolg;
+  const int64_t col0 = cg * 256 + 16 * t;
+  const bool active = col0 < K;  // uniform over the 16 lanes of a tile
+  const int64_t nstrips = M / 16;
+  const int nst = (int)((nstrips - sg * kStripsRC) < kStripsRC ? (nstrips - sg * kStripsRC) : kStripsRC);
+
+  const float A = global_amax[0];
+  float S_enc, S_dec;
+  global_scales(A, D, S_enc, S_dec);
+  const float mul = S_enc * (1.0f / 6.0f);
+  if (FOS) {
+    build_fos_tables(tab, tab + 128, 0, 126, A, D, S_dec, threadIdx.x, kRcThreads);
+    __syncthreads();
+  }
+  float* stage = xs + t * kXTile;
+
+  Raw16<InT> nxt;
+  if (active) nxt.load(x + (sg * kStripsRC * 16 + r) * K + col0);
+  for (int st = 0; st < nst; ++st) {
+    const int64_t row = (sg * kStripsRC + st) * 16 + r;
+    const Raw16<InT> cur = nxt;
+    if (active && st + 1 < nst) nxt.load(x + (row + 16) * K + col0);
+    if (active) {
+      float v[16];
+      cur.to_f32(v);
+      uint32_t c[2];
+      const uint32_t sc = FOS ? block_fos<MSE>(v, S_enc, S_dec, A, D, tab, tab + 128, c)
+                              : block_standard(v, mul, S_dec, c);
+      *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c[0], c[1]);
+      scales_row[row * (K / 16) + col0 / 16] = (uint8_t)sc;
+      float4* s4 = reinterpret_cast<float4*>(stage + r * kXRow);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s4[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    }
+    __syncthreads();
+    if (active) {
+      // lane (t, c = r) now owns column c of tile t: rows 0..15 in order
+      float v[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) v[rr] = stage[rr * kXRow + r];
+      uint32_t c[2];
+      const uint32_t sc = FOS ? block_fos<MSE>(v, S_enc, S_dec, A, D, tab, tab + 128, c)
+                              : block_standard(v, mul, S_dec, c);
+      colbuf[(16 * t + r) * kColStrideRC + st] = make_uint2(c[0], c[1]);
+      csbuf[(16 * t + r) * kColStrideRC + st] = (uint8_t)sc;
+    }
+    __syncthreads();
+  }
+  flush_columns(colbuf, csbuf, cg, sg, nst, M, K, packed_col, scales_col);
+}
+
+template <typename InT, bool MSE, bool COL>
+__global__ __launch_bounds__(kRcThreads) void k_4over6_2d(
+    const InT* __restrict__ x, const float* __restrict__ global_amax, float D, int64_t M, int64_t K,
+    uint8_t* __restrict__ packed_row, uint8_t* __restrict__ packed_col,
+    uint8_t* __restrict__ tile_scales, int64_t ncolg) {
+  __shared__ __attribute__((aligned(16))) float tab[kTabFloats];
+  __shared__ uint4 stage[16 * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (banks)
+  __shared__ uint2 colbuf[COL ? 256 * kColStrideRC : 1];
+  const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
+  const int64_t sg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - sg * ncolg;
+  const int64_t col0 = cg * 256 + 16 * t;
+  const bool active = col0 < K;
+  const int64_t nstrips = M / 16;
+  const int nst = (int)((nstrips - sg * kStripsRC) < kStripsRC ? (nstrips - sg * kStripsRC) : kStripsRC);
+
+  const float A = global_amax[0];
+  float S_enc, S_dec;
+  global_scales(A, D, S_enc, S_dec);
+  const float* rhoT = tab;
+  const float* dT = tab + 128;
+  build_fos_tables(tab, tab + 128, 0, 126, A, D, S_dec, threadIdx.x, kRcThreads);
+  __syncthreads();
+
+  Raw16<InT> nxt;
+  if (active) nxt.load(x + (sg * kStripsRC * 16 + r) * K + col0);
+  for (int st = 0; st < nst; ++st) {
+    const int64_t row0 = (sg * kStripsRC + st) * 16;
+    const int64_t row = row0 + r;
+    const Raw16<InT> cur = nxt;
+    if (active && st + 1 < nst) nxt.load(x + (row + 16) * K + col0);
+    float v[16];
+    uint32_t ab = 0;
+    if (active) {
+      cur.to_f32(v);
+      ab = absmax_bits16(v);
+    }
+    ab = row16_max(ab);
+    const bool special = ab >= 0x7F800000u;  // uniform over the tile
+    uint32_t c6[2] = {0u, 0u}, c4[2] = {0u, 0u}, k6 = 0, k4 = 0;
+    float E6 = 0.0f, E4 = 0.0f;
+    if (!special) {
+      if (active) {
+        const float sig6 = div_guarded(bits2f(ab), 6.0f, 1.0f / 6.0f) * S_enc;
+        const uint32_t kk = hw_e4m3_pair(fminf(sig6, kE4m3Max), fminf(sig6 * 1.5f, kE4m3Max)) & 0x7F7Fu;
+        k6 = kk & 0xFFu;
+        k4 = kk >> 8;
+        encode16_hw(v, rhoT[k6], c6);
+        encode16_hw(v, rhoT[k4], c4);
+        error_sums<MSE>(v, dT + k6 * kDStride, c6, dT + k4 * kDStride, c4, E6, E4);
+      }
+    } else {
+      // NaN-dropping tile amax, then the software candidates
+      float l = active ? absmax_nan_drop16(v) : 0.0f;
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) l = fmaxf(l, __shfl_xor(l, off, 64));
+      if (active) {
+        const float sig6 = (l / 6.0f) * S_enc;
+        k6 = e4m3_encode(fminf(sig6, kE4m3Max));
+        k4 = e4m3_encode(fminf(sig6 * 1.5f, kE4m3Max));
+        const float s6 = e4m3_decode(k6), s4 = e4m3_decode(k4);
+        E6 = candidate<MSE>(v, s6, encode_reciprocal(s6, S_dec), A, D, c6[0], c6[1]);
+        E4 = candidate<MSE>(v, s4, encode_reciprocal(s4, S_dec), A, D, c4[0], c4[1]);
+      }
+    }
+    E6 = tree16_sum(E6);
+    E4 = tree16_sum(E4);
+    const bool pick4 = E4 < E6;
+    const uint32_t c0 = pick4 ? c4[0] : c6[0], c1 = pick4 ? c4[1] : c6[1];
+    if (active) {
+      *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c0, c1);
+      if (r == 0) tile_scales[(row0 / 16) * (K / 16) + col0 / 16] = (uint8_t)(pick4 ? k4 : k6);
+    }
+    if (COL) {
+      if (active) {
+        stage[17 * t + r] = make_uint4(
+            (c0 & 0xFu) | ((c0 >> 4) & 0xFu) << 8 | ((c0 >> 8) & 0xFu) << 16 | ((c0 >> 12) & 0xFu) << 24,
+            ((c0 >> 16) & 0xFu) | ((c0 >> 20) & 0xFu) << 8 | ((c0 >> 24) & 0xFu) << 16 | ((c0 >> 28) & 0xFu) << 24,
+            (c1 & 0xFu) | ((c1 >> 4) & 0xFu) << 8 | ((c1 >> 8) & 0xFu) << 16 | ((c1 >> 12) & 0xFu) << 24,
+            ((c1 >> 16) & 0xFu) | ((c1 >> 20) & 0xFu) << 8 | ((c1 >> 24) & 0xFu) << 16 | ((c1 >> 28) & 0xFu) << 24);
+      }
+      __syncthreads();
+      if (active) {
+        const uint8_t* tile = reinterpret_cast<const uint8_t*>(&stage[17 * t]);
+        uint32_t o0 = 0, o1 = 0;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const uint32_t code = tile[16 * rr + r];
+          if (rr < 8) o0 |= code << (4 * rr);
+          else o1 |= code << (4 * (rr - 8));
+        }
+        colbuf[(16 * t + r) * kColStrideRC + st] = make_uint2(o0, o1);
+      }
+      __syncthreads();
+    }
+  }
+  if (COL) flush_columns(colbuf, nullptr, cg, sg, nst, M, K, packed_col, nullptr);
+}
+
+static dim3 rc_grid(int64_t M, int64_t K, int64_t& ncolg) {
+  ncolg = (K + 255) / 256;
+  const int64_t nsg = (M / 16 + kStripsRC - 1) / kStripsRC;
+  return dim3((unsigned)(ncolg * nsg));
+}
+
+template <typename InT>
+static int launch_rowcol_t(const InT* x, const float* ga, int fos, int mse, float D, int64_t M,
+                           int64_t K, uint8_t* pr, uint8_t* sr, uint8_t* pc, uint8_t* sc,
+                           hipStream_t st) {
+  int64_t ncolg;
+  const dim3 grid = rc_grid(M, K, ncolg), block(kRcThreads);
+  if (!fos)
+    hipLaunchKernelGGL((k_rowcol<InT, false, false>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
+  else if (mse)
+    hipLaunchKernelGGL((k_rowcol<InT, true, true>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
+  else
+    hipLaunchKernelGGL((k_rowcol<InT, true, false>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
+  return (int)hipGetLastError();
+}
+
+int launch_rowcol(const void* x, int in_bf16, int64_t M, int64_t K, const float* global_amax,
+                  int four_over_six, int mse, float bound, uint8_t* packed_row,
+                  uint8_t* scales_row, uint8_t* packed_col, uint8_t* scales_col, void* stream) {
+  if (M == 0 || K == 0) return 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const float D = 6.0f * bound;
+  if (in_bf16)
+    return launch_rowcol_t(reinterpret_cast<const uint16_t*>(x), global_amax, four_over_six, mse, D,
+                           M, K, packed_row, scales_row, packed_col, scales_col, st);
+  return launch_rowcol_t(reinterpret_cast<const float*>(x), global_amax, four_over_six, mse, D, M, K,
+                         packed_row, scales_row, packed_col, scales_col, st);
+}
+
+template <typename InT, bool MSE>
+static int launch_4over6_2d_t(const InT* x, const float* ga, float D, int64_t M, int64_t K,
+                              uint8_t* pr, uint8_t* pc, uint8_t* ts, hipStream_t st) {
+  int64_t ncolg;
+  const dim3 grid = rc_grid(M, K, ncolg), block(kRcThreads);
+  if (pc) hipLaunchKernelGGL((k_4over6_2d<InT, MSE, true>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg);
+  else hipLaunchKernelGGL((k_4over6_2d<InT, MSE, false>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg);
+  return (int)hipGetLastError();
+}
+
+int launch_4over6_2d(const void* x, int in_bf16, int64_t M, int64_t K, const float* global_amax,
+                     int mse, float bound, uint8_t* packed_row, uint8_t* packed_col,
+                     uint8_t* tile_scales, void* stream) {
+  if (M == 0 || K == 0) return 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const float D = 6.0f * bound;
+  if (in_bf16) {
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    return mse ? launch_4over6_2d_t<uint16_t, true>(xb, global_amax, D, M, K, packed_row, packed_col, tile_scales, st)
+               : launch_4over6_2d_t<uint16_t, false>(xb, global_amax, D, M, K, packed_row, packed_col, tile_scales, st);
+  }
+  const float* xf = reinterpret_cast<const float*>(x);
+  return mse ? launch_4over6_2d_t<float, true>(xf, global_amax, D, M, K, packed_row, packed_col, tile_scales, st)
+             : launch_4over6_2d_t<float, false>(xf, global_amax, D, M, K, packed_row, packed_col, tile_scales, st);
+}
+
+}  // namespace nvfp4

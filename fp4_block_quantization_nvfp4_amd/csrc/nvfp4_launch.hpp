@@ -23,8 +23,16 @@ int launch_4over6(const void* x, int in_bf16, int64_t M, int64_t K, float* amax,
                   void* stream);
 
 int launch_quant2d(const void* x, int in_bf16, int64_t M, int64_t K, const float* global_amax,
-                   int sr, uint32_t seed, uint32_t step, uint8_t* packed_row,
+                   int sr, uint32_t seed, uint32_t step, int round_up, uint8_t* packed_row,
                    uint8_t* packed_col, uint8_t* tile_scales, void* stream);
+
+int launch_rowcol(const void* x, int in_bf16, int64_t M, int64_t K, const float* global_amax,
+                  int four_over_six, int mse, float bound, uint8_t* packed_row,
+                  uint8_t* scales_row, uint8_t* packed_col, uint8_t* scales_col, void* stream);
+
+int launch_4over6_2d(const void* x, int in_bf16, int64_t M, int64_t K, const float* global_amax,
+                     int mse, float bound, uint8_t* packed_row, uint8_t* packed_col,
+                     uint8_t* tile_scales, void* stream);
 
 size_t amax_workspace_bytes(int64_t M, int64_t K);
 // mode: 1 tensor (two passes through workspace), 2 row.

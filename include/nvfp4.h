@@ -173,12 +173,59 @@ nvfp4_status nvfp4_quantize_4over6(const void* x, nvfp4_dtype dt, int64_t M, int
  * packed_col [K, M/2] (NULL to skip), so packed_col is the rowwise packing of
  * Q(X)^T.  Block scale: a/6 without a global scale; with global_amax (one
  * fp32 amax) the standard sigma = a * (S_enc * (1/6)), bound 448.
+ * truncation_free: 0 rounds the tile scale to the nearest e4m3 value; 1 takes
+ * the smallest e4m3 value >= sigma, so no element exceeds 6 before rounding
+ * (the paper's "truncation-free scaling"; this reading is the library's, the
+ * abstract gives no formula).
  * tile_scales [M/16, K/16] out.
  */
 nvfp4_status nvfp4_quantize_2d(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
                                const float* global_amax, nvfp4_round rnd, uint32_t seed,
-                               uint32_t step, uint8_t* packed_row, uint8_t* packed_col,
-                               uint8_t* tile_scales, void* stream);
+                               uint32_t step, int truncation_free, uint8_t* packed_row,
+                               uint8_t* packed_col, uint8_t* tile_scales, void* stream);
+
+/*
+ * nvfp4_quantize_rowcol - the forward (rowwise) and the transposed
+ * (columnwise) 1x16 NVFP4 operands of one tensor from a single read of it
+ * (the four-over-six pull request, What: the backward pass quantizes the
+ * transposed operands; Follow-up fusions: a fused row + column kernel
+ * instead of x.t().contiguous() followed by a second quantize).
+ * Round-to-nearest, one per-tensor global amax.  M % 16 == 0.
+ *   global_amax   device pointer to one fp32 amax A (required).
+ *   four_over_six 0: the standard encode, sigma = a * (S_enc * (1/6)); bound
+ *                 must be 448 and err is ignored (but must be a valid value).
+ *                 1: four-over-six per block (err, bound 256 or 448), as
+ *                 nvfp4_quantize_4over6 with mode TENSOR.
+ *   packed_row [M, K/2], scales_row [M, K/16]: blocks of 16 along K, equal
+ *                 to nvfp4_quantize (RTN) / nvfp4_quantize_4over6 of x.
+ *   packed_col [K, M/2], scales_col [K, M/16]: the same quantization of
+ *                 X^T (blocks of 16 consecutive rows of one column), laid
+ *                 out as the rowwise outputs of X^T.
+ */
+nvfp4_status nvfp4_quantize_rowcol(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
+                                   const float* global_amax, int four_over_six, nvfp4_err err,
+                                   float bound, uint8_t* packed_row, uint8_t* scales_row,
+                                   uint8_t* packed_col, uint8_t* scales_col, void* stream);
+
+/*
+ * nvfp4_quantize_4over6_2d - four-over-six on 16x16 tiles with one
+ * per-tensor global amax (the four-over-six pull request, What: block
+ * "16x16" with a scalar global_amax; CuTe DSL kernel Design: each tile row
+ * sums its 16 errors in element order, the 16 row sums are combined by the
+ * exact width-16 tree, map-to-4 iff its tile error is strictly lower).  One
+ * scale per tile shared by X and X^T (transposition-invariant paper,
+ * abstract), so the columnwise codes are the rowwise codes transposed.
+ * M % 16 == 0.
+ *   global_amax   device pointer to one fp32 amax A (required).
+ *   err, bound    NVFP4_MAE / NVFP4_MSE; 256 or 448.
+ *   packed_row [M, K/2]; packed_col [K, M/2] or NULL to skip;
+ *   tile_scales [M/16, K/16].  Dequantize with nvfp4_dequantize(tile16 = 1,
+ *   NVFP4_SCALE_TENSOR, bound).
+ */
+nvfp4_status nvfp4_quantize_4over6_2d(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
+                                      const float* global_amax, nvfp4_err err, float bound,
+                                      uint8_t* packed_row, uint8_t* packed_col,
+                                      uint8_t* tile_scales, void* stream);
 
 #ifdef __cplusplus
 }

@@ -73,8 +73,28 @@ def test_other_entry_points_reject():
     assert lib.nvfp4_quantize_4over6(A, L.BF16, 4, 32, A, 1, 0, 0, 256.0, A, A, None) == L.E_ARG
     assert lib.nvfp4_quantize_4over6(A, L.BF16, 4, 32, None, 2, 0, 0, 256.0, A, A, None) == L.E_NULL
     # 2D: M % 16
-    assert lib.nvfp4_quantize_2d(A, L.BF16, 24, 32, None, 0, 0, 0, A, A, A, None) == L.E_SHAPE
-    assert lib.nvfp4_quantize_2d(A, L.BF16, 32, 32, None, 0, 0, 0, None, A, A, None) == L.E_NULL
+    assert lib.nvfp4_quantize_2d(A, L.BF16, 24, 32, None, 0, 0, 0, 0, A, A, A, None) == L.E_SHAPE
+    assert lib.nvfp4_quantize_2d(A, L.BF16, 32, 32, None, 0, 0, 0, 0, None, A, A, None) == L.E_NULL
+    assert lib.nvfp4_quantize_2d(A, L.BF16, 32, 32, None, 0, 0, 0, 2, A, A, A, None) == L.E_ARG
+    # rowcol: M % 16, standard path needs bound 448, four-over-six 256/448, amax required
+    rc = lib.nvfp4_quantize_rowcol
+    assert rc(A, L.BF16, 24, 32, A, 0, 0, 448.0, A, A, A, A, None) == L.E_SHAPE
+    assert rc(A, L.BF16, 32, 32, A, 0, 0, 256.0, A, A, A, A, None) == L.E_ARG
+    assert rc(A, L.BF16, 32, 32, A, 1, 0, 300.0, A, A, A, A, None) == L.E_ARG
+    assert rc(A, L.BF16, 32, 32, A, 2, 0, 448.0, A, A, A, A, None) == L.E_ARG
+    assert rc(A, L.BF16, 32, 32, A, 1, 4, 256.0, A, A, A, A, None) == L.E_ARG
+    assert rc(A, L.BF16, 32, 32, None, 1, 0, 256.0, A, A, A, A, None) == L.E_NULL
+    assert rc(A, L.BF16, 32, 32, A, 1, 0, 256.0, A, A, None, A, None) == L.E_NULL
+    assert rc(A, L.BF16, 32, 32, A, 1, 0, 256.0, A, A, A + 4, A, None) == L.E_ALIGN
+    assert rc(None, L.BF16, 0, 32, None, 1, 0, 256.0, None, None, None, None, None) == L.OK
+    # four-over-six 16x16: M % 16, bound, err, amax required, column output optional
+    f2 = lib.nvfp4_quantize_4over6_2d
+    assert f2(A, L.BF16, 8, 32, A, 0, 256.0, A, A, A, None) == L.E_SHAPE
+    assert f2(A, L.BF16, 16, 32, A, 0, 100.0, A, A, A, None) == L.E_ARG
+    assert f2(A, L.BF16, 16, 32, A, 2, 256.0, A, A, A, None) == L.E_ARG
+    assert f2(A, L.BF16, 16, 32, None, 0, 256.0, A, A, A, None) == L.E_NULL
+    assert f2(A, L.BF16, 16, 32, A, 0, 256.0, A, A, None, None) == L.E_NULL
+    assert f2(A, 3, 16, 32, A, 0, 256.0, A, A, A, None) == L.E_DTYPE
     # amax: workspace too small / missing, bad mode
     need = lib.nvfp4_amax_workspace_bytes(1024, 1024)
     assert need >= 4

@@ -1,0 +1,144 @@
+"""GPU vs CPU-oracle parity (bitwise) for the fused rowwise + columnwise 1x16
+quantization and for four-over-six on 16x16 tiles with rowwise and
+columnwise outputs, through the C ABI.
+
+Shapes span several workgroups along both axes (a workgroup covers 256
+columns and 128 rows), ragged column tails (K not a multiple of 256) and
+single-tile tensors."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp4_block_quantization_nvfp4_amd as nv
+from tests.gpu_util import assert_bitwise, need_gpu, to_dev, to_np, wide_input
+from tests.test_gpu_parity import _specials
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(16, 16), (64, 96), (304, 304), (128, 4112), (272, 1040), (48, 512)]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _ga(A):
+    return torch.tensor([A], dtype=torch.float32, device="cuda")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("variant", ["std", "fos256-mae", "fos256-mse", "fos448-mae"])
+def test_rowcol(shape, bf16, variant):
+    M, K = shape
+    x = wide_input(M * 7 + K, M, K, bf16, lo=-6, hi=6)
+    A = oracle.amax(x)
+    fos = variant != "std"
+    bound = 448.0 if variant in ("std", "fos448-mae") else 256.0
+    err = "mse" if variant.endswith("mse") else "mae"
+    wpr, wsr, wpc, wsc = oracle.quantize_rowcol(x, A, four_over_six=fos, err_mode=err, bound=bound)
+    pr, sr, pc, sc = nv.quantize_rowcol(to_dev(x), _ga(A), four_over_six=fos, err_mode=err,
+                                        e4m3_scale_bound=bound)
+    assert_bitwise(to_np(sr), wsr, "row scales")
+    assert_bitwise(to_np(pr), wpr, "row codes")
+    assert_bitwise(to_np(sc), wsc, "col scales")
+    assert_bitwise(to_np(pc), wpc, "col codes")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("err", ["mae", "mse"])
+@pytest.mark.parametrize("bound", [256.0, 448.0])
+def test_4over6_2d(shape, bf16, err, bound):
+    M, K = shape
+    x = wide_input(M * 3 + K + 1, M, K, bf16, lo=-6, hi=6)
+    A = oracle.amax(x)
+    wpr, wpc, wts = oracle.quantize_4over6_2d(x, A, err_mode=err, bound=bound)
+    pr, pc, ts = nv.quantize_4over6_2d(to_dev(x), _ga(A), err_mode=err, e4m3_scale_bound=bound)
+    assert_bitwise(to_np(ts), wts, "tile scales")
+    assert_bitwise(to_np(pr), wpr, "row codes")
+    assert_bitwise(to_np(pc), wpc, "col codes")
+    pr2, pc2, ts2 = nv.quantize_4over6_2d(to_dev(x), _ga(A), err_mode=err, e4m3_scale_bound=bound,
+                                          columnwise=False)
+    assert pc2 is None
+    assert_bitwise(to_np(pr2), wpr, "row codes (no col)")
+    assert_bitwise(to_np(ts2), wts, "tile scales (no col)")
+    want = oracle.dequantize(wpr, wts, M, K, tile16=True, global_amax=A, scale_mode="tensor",
+                             bound=bound, out="f32")
+    got = nv.dequantize(pr, ts, M, K, tile16=True, global_amax=_ga(A), bound=bound,
+                        out_dtype=torch.float32)
+    assert_bitwise(to_np(got), want, "tile dequant")
+
+
+def _mixed_tiles():
+    """Gaussian tiles, and every other tile column made of values on the
+    map-to-4 grid (amax times 1, .75, .5, .375, .25, .125 or 0), which map-to-4
+    represents exactly and map-to-6 does not, so both candidates win tiles."""
+    import workloads
+    x = oracle.bf16_bits_to_f32(wide_input(11, 256, 512, True, lo=-2, hi=2)).copy()
+    rng = np.random.default_rng(12)
+    lv = np.array([1, 0.75, 0.5, 0.375, 0.25, 0.125, 0], np.float32)
+    t = x.reshape(16, 16, 32, 16)
+    for i in range(16):
+        for j in range(0, 32, 2):
+            s = np.float32(2.0 ** rng.integers(-3, 4))
+            t[i, :, j, :] = rng.choice(lv, (16, 16)) * s * rng.choice(np.array([-1, 1], np.float32), (16, 16))
+            t[i, 0, j, 0] = s
+    return workloads.bf16_bits(x)
+
+
+@pytest.mark.parametrize("err", ["mae", "mse"])
+def test_4over6_2d_picks_both_candidates(err):
+    x = _mixed_tiles()
+    A = oracle.amax(x)
+    wpr, wpc, wts = oracle.quantize_4over6_2d(x, A, err_mode=err)
+    a = oracle.nvfp4._nan_drop_absmax(oracle.bf16_bits_to_f32(x).reshape(16, 16, 32, 16), axis=(1, 3))
+    S_enc = oracle.nvfp4.global_scales(A, 256.0)[0]
+    k6 = oracle.e4m3_encode(np.fmin((a / np.float32(6)) * S_enc, np.float32(448)))
+    assert (wts == k6).sum() > 100 and (wts != k6).sum() > 100
+    pr, pc, ts = nv.quantize_4over6_2d(to_dev(x), _ga(A), err_mode=err)
+    assert_bitwise(to_np(ts), wts)
+    assert_bitwise(to_np(pr), wpr)
+    assert_bitwise(to_np(pc), wpc)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_specials_rowcol_and_4over6_2d(bf16):
+    x = _specials(bf16)
+    xd = to_dev(x)
+    for A in (oracle.amax(x), np.float32(3000.0), np.float32(0.0)):
+        for fos, bound in ((False, 448.0), (True, 256.0)):
+            for err in ("mae", "mse"):
+                want = oracle.quantize_rowcol(x, A, four_over_six=fos, err_mode=err, bound=bound)
+                got = nv.quantize_rowcol(xd, _ga(A), four_over_six=fos, err_mode=err,
+                                         e4m3_scale_bound=bound)
+                for g, w, what in zip(got, want, ("pr", "sr", "pc", "sc")):
+                    assert_bitwise(to_np(g), w, f"rowcol {what} A={A} fos={fos} {err}")
+        for err in ("mae", "mse"):
+            wpr, wpc, wts = oracle.quantize_4over6_2d(x, A, err_mode=err)
+            pr, pc, ts = nv.quantize_4over6_2d(xd, _ga(A), err_mode=err)
+            assert_bitwise(to_np(ts), wts, f"2d scales A={A} {err}")
+            assert_bitwise(to_np(pr), wpr, f"2d rows A={A} {err}")
+            assert_bitwise(to_np(pc), wpc, f"2d cols A={A} {err}")
+
+
+def test_rowcol_standard_matches_quantize_and_transpose():
+    x = wide_input(21, 160, 272, True, lo=-5, hi=5)
+    A = _ga(oracle.amax(x))
+    pr, sr, pc, sc = nv.quantize_rowcol(to_dev(x), A)
+    p, s = nv.quantize(to_dev(x), global_amax=A)
+    assert_bitwise(to_np(pr), to_np(p))
+    assert_bitwise(to_np(sr), to_np(s))
+    pt, st = nv.quantize(to_dev(np.ascontiguousarray(x.T)), global_amax=A)
+    assert_bitwise(to_np(pc), to_np(pt))
+    assert_bitwise(to_np(sc), to_np(st))
+
+
+def test_empty_next():
+    x = torch.empty((0, 32), dtype=torch.bfloat16, device="cuda")
+    pr, sr, pc, sc = nv.quantize_rowcol(x, 1.0)
+    assert pr.shape == (0, 16) and pc.shape == (32, 0) and sc.shape == (32, 0)
+    pr, pc, ts = nv.quantize_4over6_2d(x, 1.0)
+    assert ts.shape == (0, 2)

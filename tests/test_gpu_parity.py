@@ -124,17 +124,20 @@ def test_four_over_six(shape, bf16, err_mode, bound, mode):
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("stochastic", [False, True])
 @pytest.mark.parametrize("global_scale", [False, True])
-def test_quantize_2d(shape, bf16, stochastic, global_scale):
+@pytest.mark.parametrize("tf", [False, True], ids=["nearest", "truncfree"])
+def test_quantize_2d(shape, bf16, stochastic, global_scale, tf):
     M, K = shape
     x = wide_input(M * 5 + K, M, K, bf16, lo=-8, hi=8)
     A = oracle.amax(x) if global_scale else None
-    wr, wc, ws = oracle.quantize_2d(x, stochastic=stochastic, seed=4, step=9, global_amax=A)
+    wr, wc, ws = oracle.quantize_2d(x, stochastic=stochastic, seed=4, step=9, global_amax=A,
+                                    truncation_free=tf)
     ga = torch.tensor([A], device="cuda") if global_scale else None
-    r, c, s = nv.quantize_2d(to_dev(x), ga, stochastic=stochastic, seed=4, step=9)
+    r, c, s = nv.quantize_2d(to_dev(x), ga, stochastic=stochastic, seed=4, step=9, truncation_free=tf)
     assert_bitwise(to_np(s), ws, "tile scales")
     assert_bitwise(to_np(r), wr, "rowwise")
     assert_bitwise(to_np(c), wc, "columnwise")
-    r2, c2, s2 = nv.quantize_2d(to_dev(x), ga, stochastic=stochastic, seed=4, step=9, columnwise=False)
+    r2, c2, s2 = nv.quantize_2d(to_dev(x), ga, stochastic=stochastic, seed=4, step=9, columnwise=False,
+                                truncation_free=tf)
     assert c2 is None
     assert_bitwise(to_np(r2), wr, "rowwise (no col)")
     want = oracle.dequantize(wr, ws, M, K, tile16=True, global_amax=A,
@@ -187,12 +190,14 @@ def test_special_values(bf16):
         assert_bitwise(to_np(out), oracle.qdq(x, stochastic=st, seed=5)[0], "qdq")
     # 2D with a global amax of inf (x has an inf) and without
     for ga_on in (False, True):
-        A = oracle.amax(x) if ga_on else None
-        wr, wc, wts = oracle.quantize_2d(x, global_amax=A)
-        r, c, ts = nv.quantize_2d(xd, torch.tensor([A], device="cuda") if ga_on else None)
-        assert_bitwise(to_np(ts), wts)
-        assert_bitwise(to_np(r), wr)
-        assert_bitwise(to_np(c), wc)
+        for tf in (False, True):
+            A = oracle.amax(x) if ga_on else None
+            wr, wc, wts = oracle.quantize_2d(x, global_amax=A, truncation_free=tf)
+            r, c, ts = nv.quantize_2d(xd, torch.tensor([A], device="cuda") if ga_on else None,
+                                      truncation_free=tf)
+            assert_bitwise(to_np(ts), wts)
+            assert_bitwise(to_np(r), wr)
+            assert_bitwise(to_np(c), wc)
     # four-over-six: per-row amax with NaN/inf rows, amax == 0 rows
     A = oracle.amax(x, mode="row")
     for err in ("mae", "mse"):

@@ -65,19 +65,25 @@ def dev_bf16(torch, np, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def time_ms(torch, fn, warmup, steps):
+def time_ms(torch, fn, warmup, steps, host=None):
     """Average ms per call over `steps` calls on torch's current stream
-    (the stream every C-ABI call here is issued on), after `warmup` calls."""
+    (the stream every C-ABI call here is issued on), after `warmup` calls.
+    If `host` is a dict, host["us_per_call"] receives the host-side time to
+    submit one call (the loop without the final synchronization)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
+    h0 = time.perf_counter()
     for i in range(steps):
         fn(i)
+    h1 = time.perf_counter()
     t1.record()
     torch.cuda.synchronize()
+    if host is not None:
+        host["us_per_call"] = (h1 - h0) * 1e6 / steps
     return t0.elapsed_time(t1) / steps
 
 
@@ -136,11 +142,14 @@ def main():
     scales = [torch.empty((M, K // 16), dtype=torch.uint8, device="cuda") for _ in range(N_SETS)]
     amaxes = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in range(N_SETS)]
 
+    fn = lib.nvfp4_quantize_4over6
+    call_args = [(xs[j].data_ptr(), L.BF16, M, K, amaxes[j].data_ptr(), L.SCALE_ROW, 0, err, bound,
+                  packed[j].data_ptr(), scales[j].data_ptr(), stream) for j in range(N_SETS)]
+
     def step(i):
-        j = i % N_SETS
-        L.check(lib.nvfp4_quantize_4over6(xs[j].data_ptr(), L.BF16, M, K, amaxes[j].data_ptr(),
-                                          L.SCALE_ROW, 0, err, bound, packed[j].data_ptr(),
-                                          scales[j].data_ptr(), stream), "nvfp4_quantize_4over6")
+        status = fn(*call_args[i % N_SETS])
+        if status:
+            L.check(status, "nvfp4_quantize_4over6")
 
     # parity before timing (sampled rows; rows are independent on this path)
     import oracle
@@ -154,7 +163,8 @@ def main():
     check_rows(np, packed[0].cpu().numpy()[rows], wp, "codes")
     check_rows(np, scales[0].cpu().numpy()[rows], ws, "scales")
 
-    ms = time_ms(torch, step, args.warmup, args.steps)
+    host = {}
+    ms = time_ms(torch, step, args.warmup, args.steps, host)
     algo = M * K * 2 + M * K // 2 + M * K // 16  # 150,470,656 B
     gbs = algo / (ms * 1e-3) / 1e9
     traffic = read_traffic(algo)
@@ -190,6 +200,7 @@ def main():
             "kernel": "k_4over6 (row amax computed in-pass)",
             "algorithmic_bytes_per_launch": algo,
             "avg_launch_us": round(ms * 1e3, 3),
+            "host_submit_us_per_launch": round(host["us_per_call"], 3),
         },
     }
 
@@ -283,6 +294,33 @@ def extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle, steps, war
     n2 = Mt * Kt
     rec("weight_2d_7168x18432_quantize_2d_sr", ms_2d, n2 * 2 + n2 // 2 + n2 // 2 + n2 // 256,
         "fused pass: bf16 in, rowwise + columnwise codes, tile scales")
+    ms_tf = time_ms(torch, lambda i: lib.nvfp4_quantize_2d(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(), 1, 0, 0, 1,
+                                                            pr[i % 2].data_ptr(), pc[i % 2].data_ptr(),
+                                                            ts[i % 2].data_ptr(), stream), warmup, steps)
+    rec("weight_2d_7168x18432_quantize_2d_sr_truncation_free", ms_tf, n2 * 2 + n2 // 2 + n2 // 2 + n2 // 256,
+        "as above, tile scale rounded up")
+    ms_46 = time_ms(torch, lambda i: lib.nvfp4_quantize_4over6_2d(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(),
+                                                                   L.MAE, 256.0, pr[i % 2].data_ptr(),
+                                                                   pc[i % 2].data_ptr(), ts[i % 2].data_ptr(),
+                                                                   stream), warmup, steps)
+    wr, wc, wt = oracle.quantize_4over6_2d(wb[rows], A, err_mode="mae", bound=256.0)
+    check_rows(np, pr[1].cpu().numpy()[rows], wr, "4over6 2d rowwise")
+    check_rows(np, ts[1].cpu().numpy()[:4], wt, "4over6 2d tiles")
+    rec("weight_2d_7168x18432_4over6_16x16_mae", ms_46, n2 * 2 + n2 // 2 + n2 // 2 + n2 // 256,
+        "four-over-six on 16x16 tiles, rowwise + columnwise codes, tile scales")
+    srow = torch.empty((Mt, Kt // 16), dtype=torch.uint8, device="cuda")
+    scol = torch.empty((Kt, Mt // 16), dtype=torch.uint8, device="cuda")
+    for fos in (0, 1):
+        bnd = 256.0 if fos else 448.0
+        ms_rc = time_ms(torch, lambda i: lib.nvfp4_quantize_rowcol(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(),
+                                                                    fos, L.MAE, bnd, pr[i % 2].data_ptr(),
+                                                                    srow.data_ptr(), pc[i % 2].data_ptr(),
+                                                                    scol.data_ptr(), stream), warmup, steps)
+        wpr, wsr, wpc, wsc = oracle.quantize_rowcol(wb[rows], A, four_over_six=bool(fos), bound=bnd)
+        check_rows(np, pr[1].cpu().numpy()[rows], wpr, "rowcol rowwise")
+        check_rows(np, scol.cpu().numpy()[:, :4], wsc, "rowcol col scales")
+        rec(f"weight_2d_7168x18432_rowcol_1x16_{'4over6_mae' if fos else 'standard'}", ms_rc,
+            n2 * 2 + n2 + n2 // 8, "bf16 in, rowwise + columnwise codes and 1x16 scales")
     rec("weight_2d_7168x18432_amax", ms_amax, n2 * 2, "per-tensor amax, two passes")
     rec("weight_2d_7168x18432_amax_plus_2d", ms_amax + ms_2d, n2 * 2 * 2 + n2 + n2 // 256, "end to end")
     del wd, pr, pc, ts

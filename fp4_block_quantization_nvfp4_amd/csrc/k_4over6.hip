@@ -88,26 +88,22 @@ __global__ __launch_bounds__(k46MaxThreads) void k_4over6(const InT* __restrict_
 
 // ---------------------------------------------------------------------------
 // Row-per-workgroup kernel for bf16 input (K <= 16384).  Same numerics as
-// above, with three exact rewrites of the per-element work:
+// above, with exact rewrites of the per-element work:
 //  * e2m1 encode by the gfx950 packed fp32 -> fp4 conversion (scale 1.0),
 //    which rounds to nearest-even and saturates at +-6 exactly like the
 //    software encoder for every finite and infinite input (checked on all
-//    2^32 fp32 values); it differs only for negative NaN, so blocks holding a
-//    NaN or an infinity take the software path.
-//  * The error-path dequant d = ((val * s) * A) / D depends only on the
-//    block's scale code and the code's magnitude, so the workgroup builds a
-//    table of d (and of the encode reciprocals rho) in LDS once per row, for
-//    the span of scale codes the row uses; an element's d is one LDS read.
-//    The block scale bytes come from the hardware fp32 -> e4m3 conversion,
-//    which equals the software round-to-nearest-even encoder on every fp32
-//    value in [0, 448] (checked exhaustively).
-//  * Divisions by 6 and by D use reciprocal-multiply plus one exact FMA
-//    remainder correction, which is correctly rounded for every float32
-//    numerator of magnitude >= 2^-117 (verified exhaustively on the host);
-//    smaller numerators take the true division.
+//    2^32 fp32 values); the block scale bytes come from the hardware
+//    fp32 -> e4m3 conversion, equal to the software encoder on [0, 448].
+//  * The candidate choice is certified from error sums in the scaled
+//    domain (fos_block); only undecided blocks compute the per-element
+//    dequant values with true divisions.
+//  * The encode reciprocals of all 127 scale codes are tabulated in LDS once
+//    per row (one correctly rounded reciprocal per lane).
+//  * a / 6 uses reciprocal-multiply plus one exact FMA remainder correction
+//    where that is proven correctly rounded, else the true division.
 // A two-wave workgroup owns one row: it loads the row (R blocks per lane)
-// into registers, reduces the row amax, builds the tables, then encodes its
-// blocks.
+// into registers, reduces the row amax (when it is computed here), builds
+// the reciprocal table, then encodes its blocks.
 
 typedef unsigned short nv_us2 __attribute__((ext_vector_type(2)));
 
@@ -164,15 +160,8 @@ NV_DEV uint32_t wave_max_pk_u16(uint32_t v) {
   return pk_max_u16(pk_max_u16(r0, r1), pk_max_u16(r2, r3));
 }
 
-// A block takes the table-free software path when it holds a NaN or an
-// infinity, is all zero, or has an amax so small that a / 6 leaves the range
-// where the fast division is verified.
-NV_DEV bool slow_block(uint32_t ab) { return ab >= 0x7F80u || ab < 0x0500u; }
-
 // One workgroup of kRowThreads lanes (two waves) per row; lane t owns blocks
-// t, t + kRowThreads, ... (R per lane).  Reductions run inside each wave with
-// DPP and lane reads, then across the two waves through LDS; three workgroup
-// barriers per row (row amax, span of scale codes, tables built).
+// t, t + kRowThreads, ... (R per lane).
 constexpr int kRowThreads = 128;
 
 template <bool MSE, int MODE, int R>
@@ -181,10 +170,8 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
                                                              int64_t M, int64_t K,
                                                              uint8_t* __restrict__ packed,
                                                              uint8_t* __restrict__ scales) {
-  __shared__ __attribute__((aligned(32))) float tab[kTabFloats];
-  __shared__ uint32_t red[2][kRowThreads / 64];
-  float* rhoT = tab;
-  float* dT = tab + 128;
+  __shared__ float rhoT[128];
+  __shared__ uint32_t red[kRowThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const int nbk = (int)(K >> 4);
@@ -203,15 +190,14 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
       raw[j][1] = make_uint4(0, 0, 0, 0);
     }
   }
-  // info[j]: bits 0..15 the block's bf16 absmax pattern (NaN included),
-  // then bits 16..31 the two scale codes.
-  uint32_t info[R];
+  // NaN-dropping block amaxes as bf16 bit patterns
+  uint32_t ab[R];
   uint32_t lane_max = 0;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    info[j] = absmax_bits(raw[j][0], raw[j][1]);
-    const uint32_t ab = info[j] > 0x7F80u ? absmax_bits_nan_drop(raw[j][0], raw[j][1]) : info[j];
-    lane_max = ab > lane_max ? ab : lane_max;
+    ab[j] = absmax_bits(raw[j][0], raw[j][1]);
+    if (ab[j] > 0x7F80u) ab[j] = absmax_bits_nan_drop(raw[j][0], raw[j][1]);
+    lane_max = ab[j] > lane_max ? ab[j] : lane_max;
   }
 
   float A;
@@ -221,76 +207,33 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
     A = amax[row];
   } else {
     const uint32_t wm = wave_max_pk_u16(lane_max);
-    if (lane == 0) red[0][wave] = wm;
+    if (lane == 0) red[wave] = wm;
     __syncthreads();
-    const uint32_t m = pk_max_u16(red[0][0], red[0][1]);
+    const uint32_t m = pk_max_u16(red[0], red[1]);
     A = bits2f((m & 0xFFFFu) << 16);
     if (tid == 0) amax[row] = A;
   }
   float S_enc, S_dec;
   global_scales(A, D, S_enc, S_dec);
-
-  // Scale codes of both candidates per block (hardware e4m3 conversion,
-  // round-to-nearest-even; sigma is capped to [0, 448] first) and the span of
-  // codes used by the row's fast blocks, reduced as (255 - kmin, kmax).
-  uint32_t span = 0u;
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    const float a = bits2f(info[j] << 16);
-    const float sig6r = div_fast(a, 6.0f, 1.0f / 6.0f) * S_enc;
-    const float sig4r = sig6r * 1.5f;
-    // (masked to 7 bits: only a negative given amax, which is invalid input,
-    // could set the sign bit; the mask keeps table indexes in range)
-    const uint32_t kk = hw_e4m3_pair(fminf(sig6r, kE4m3Max), fminf(sig4r, kE4m3Max)) & 0x7F7Fu;
-    const bool fast = (tid + kRowThreads * j < nbk) && !slow_block(info[j]);
-    if (fast) span = pk_max_u16(span, ((0xFFu - (kk & 0xFFu)) << 16) | ((kk >> 8) & 0xFFu));
-    info[j] |= kk << 16;
-  }
-  const uint32_t ws = wave_max_pk_u16(span);
-  if (lane == 0) red[1][wave] = ws;
-  __syncthreads();
-  const uint32_t sp = pk_max_u16(red[1][0], red[1][1]);
-  const int kmin = 0xFF - (int)(sp >> 16), kmax = (int)(sp & 0xFFFFu);
-
-  build_fos_tables(rhoT, dT, kmin, kmax, A, D, S_dec, tid, kRowThreads);
+  if (tid < 127) rhoT[tid] = encode_reciprocal(hw_e4m3_value<0>((uint32_t)tid), S_dec);
   __syncthreads();
 
+  // with the row's own amax (computed here) and a row in range, blocks take
+  // the lean fos_block_row; otherwise the general fos_block
+  const bool lean = MODE == 3 && fos_row_in_range(A, S_dec);
+  uint2* prow = reinterpret_cast<uint2*>(packed) + row * nbk;
+  uint8_t* srow = scales + row * nbk;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const int b = tid + kRowThreads * j;
     if (b >= nbk) continue;
-    const int64_t blk = row * nbk + b;
     float xv[16];
     unpack16(raw[j][0], raw[j][1], xv);
-    const uint32_t ab = info[j] & 0xFFFFu;
-    uint2 out;
-    uint32_t sbyte;
-    if (slow_block(ab)) {
-      const float a = bits2f((ab > 0x7F80u ? absmax_bits_nan_drop(raw[j][0], raw[j][1]) : ab) << 16);
-      const float sig6r = (a / 6.0f) * S_enc;
-      const float sig4r = sig6r * 1.5f;
-      const uint32_t k6 = e4m3_encode(fminf(sig6r, kE4m3Max));
-      const uint32_t k4 = e4m3_encode(fminf(sig4r, kE4m3Max));
-      const float s6 = e4m3_decode(k6), s4 = e4m3_decode(k4);
-      uint32_t a0, a1, b0, b1;
-      const float E6 = candidate<MSE>(xv, s6, encode_reciprocal(s6, S_dec), A, D, a0, a1);
-      const float E4 = candidate<MSE>(xv, s4, encode_reciprocal(s4, S_dec), A, D, b0, b1);
-      const bool pick4 = E4 < E6;
-      out = pick4 ? make_uint2(b0, b1) : make_uint2(a0, a1);
-      sbyte = pick4 ? k4 : k6;
-    } else {
-      const uint32_t k6 = (info[j] >> 16) & 0xFFu, k4 = info[j] >> 24;
-      uint32_t c6[2], c4[2];
-      encode16_hw(xv, rhoT[k6], c6);
-      encode16_hw(xv, rhoT[k4], c4);
-      float E6, E4;
-      error_sums<MSE>(xv, dT + k6 * kDStride, c6, dT + k4 * kDStride, c4, E6, E4);
-      const bool pick4 = E4 < E6;
-      out = pick4 ? make_uint2(c4[0], c4[1]) : make_uint2(c6[0], c6[1]);
-      sbyte = pick4 ? k4 : k6;
-    }
-    reinterpret_cast<uint2*>(packed)[blk] = out;
-    scales[blk] = (uint8_t)sbyte;
+    uint32_t c[2];
+    const uint32_t sbyte = lean ? fos_block_row<MSE>(xv, ab[j], S_enc, S_dec, A, D, rhoT, c)
+                                : fos_block<MSE>(xv, bits2f(ab[j] << 16), S_enc, S_dec, A, D, rhoT, c);
+    prow[b] = make_uint2(c[0], c[1]);
+    srow[b] = (uint8_t)sbyte;
   }
 }
 

@@ -98,38 +98,14 @@ NV_DEV uint32_t block_standard(const float v[16], float mul, float S_dec, uint32
   return sc;
 }
 
-// Four-over-six 1x16 block; returns the chosen scale byte, codes in c.
+// Four-over-six 1x16 block (certified choice, exact fallback); returns the
+// chosen scale byte, codes in c.
 template <bool MSE>
 NV_DEV uint32_t block_fos(const float v[16], float S_enc, float S_dec, float A, float D,
-                          const float* rhoT, const float* dT, uint32_t c[2]) {
+                          const float* rhoT, uint32_t c[2]) {
   const uint32_t ab = absmax_bits16(v);
-  if (ab < 0x7F800000u) {
-    const float sig6 = div_guarded(bits2f(ab), 6.0f, 1.0f / 6.0f) * S_enc;
-    // (the mask only matters for a negative amax, which is invalid input: it
-    // keeps the table index in range)
-    const uint32_t kk = hw_e4m3_pair(fminf(sig6, kE4m3Max), fminf(sig6 * 1.5f, kE4m3Max)) & 0x7F7Fu;
-    const uint32_t k6 = kk & 0xFFu, k4 = kk >> 8;
-    uint32_t c6[2], c4[2];
-    encode16_hw(v, rhoT[k6], c6);
-    encode16_hw(v, rhoT[k4], c4);
-    float E6, E4;
-    error_sums<MSE>(v, dT + k6 * kDStride, c6, dT + k4 * kDStride, c4, E6, E4);
-    const bool pick4 = E4 < E6;
-    c[0] = pick4 ? c4[0] : c6[0];
-    c[1] = pick4 ? c4[1] : c6[1];
-    return pick4 ? k4 : k6;
-  }
-  const float sig6 = (absmax_nan_drop16(v) / 6.0f) * S_enc;
-  const uint32_t k6 = e4m3_encode(fminf(sig6, kE4m3Max));
-  const uint32_t k4 = e4m3_encode(fminf(sig6 * 1.5f, kE4m3Max));
-  const float s6 = e4m3_decode(k6), s4 = e4m3_decode(k4);
-  uint32_t a0, a1, b0, b1;
-  const float E6 = candidate<MSE>(v, s6, encode_reciprocal(s6, S_dec), A, D, a0, a1);
-  const float E4 = candidate<MSE>(v, s4, encode_reciprocal(s4, S_dec), A, D, b0, b1);
-  const bool pick4 = E4 < E6;
-  c[0] = pick4 ? b0 : a0;
-  c[1] = pick4 ? b1 : a1;
-  return pick4 ? k4 : k6;
+  const float a = ab < 0x7F800000u ? bits2f(ab) : absmax_nan_drop16(v);
+  return fos_block<MSE>(v, a, S_enc, S_dec, A, D, rhoT, c);
 }
 
 // Raw input of 16 elements (uint4 words) and its conversion to fp32.
@@ -169,7 +145,7 @@ __global__ __launch_bounds__(kRcThreads) void k_rowcol(
   __shared__ __attribute__((aligned(16))) float xs[16 * kXTile];
   __shared__ uint2 colbuf[256 * kColStrideRC];
   __shared__ uint8_t csbuf[256 * kColStrideRC];
-  __shared__ __attribute__((aligned(16))) float tab[FOS ? kTabFloats : 1];
+  __shared__ float rhoT[FOS ? 128 : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
   const int64_t sg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - sg * ncolg;
   const int64_t col0 = cg * 256 + 16 * t;
@@ -182,7 +158,7 @@ __global__ __launch_bounds__(kRcThreads) void k_rowcol(
   global_scales(A, D, S_enc, S_dec);
   const float mul = S_enc * (1.0f / 6.0f);
   if (FOS) {
-    build_fos_tables(tab, tab + 128, 0, 126, A, D, S_dec, threadIdx.x, kRcThreads);
+    if (threadIdx.x < 127) rhoT[threadIdx.x] = encode_reciprocal(e4m3_decode(threadIdx.x), S_dec);
     __syncthreads();
   }
   float* stage = xs + t * kXTile;
@@ -197,7 +173,7 @@ __global__ __launch_bounds__(kRcThreads) void k_rowcol(
       float v[16];
       cur.to_f32(v);
       uint32_t c[2];
-      const uint32_t sc = FOS ? block_fos<MSE>(v, S_enc, S_dec, A, D, tab, tab + 128, c)
+      const uint32_t sc = FOS ? block_fos<MSE>(v, S_enc, S_dec, A, D, rhoT, c)
                               : block_standard(v, mul, S_dec, c);
       *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c[0], c[1]);
       scales_row[row * (K / 16) + col0 / 16] = (uint8_t)sc;
@@ -212,7 +188,7 @@ __global__ __launch_bounds__(kRcThreads) void k_rowcol(
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) v[rr] = stage[rr * kXRow + r];
       uint32_t c[2];
-      const uint32_t sc = FOS ? block_fos<MSE>(v, S_enc, S_dec, A, D, tab, tab + 128, c)
+      const uint32_t sc = FOS ? block_fos<MSE>(v, S_enc, S_dec, A, D, rhoT, c)
                               : block_standard(v, mul, S_dec, c);
       colbuf[(16 * t + r) * kColStrideRC + st] = make_uint2(c[0], c[1]);
       csbuf[(16 * t + r) * kColStrideRC + st] = (uint8_t)sc;
@@ -227,7 +203,7 @@ __global__ __launch_bounds__(kRcThreads) void k_4over6_2d(
     const InT* __restrict__ x, const float* __restrict__ global_amax, float D, int64_t M, int64_t K,
     uint8_t* __restrict__ packed_row, uint8_t* __restrict__ packed_col,
     uint8_t* __restrict__ tile_scales, int64_t ncolg) {
-  __shared__ __attribute__((aligned(16))) float tab[kTabFloats];
+  __shared__ float rhoT[128];
   __shared__ uint4 stage[16 * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (banks)
   __shared__ uint2 colbuf[COL ? 256 * kColStrideRC : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
@@ -240,9 +216,7 @@ __global__ __launch_bounds__(kRcThreads) void k_4over6_2d(
   const float A = global_amax[0];
   float S_enc, S_dec;
   global_scales(A, D, S_enc, S_dec);
-  const float* rhoT = tab;
-  const float* dT = tab + 128;
-  build_fos_tables(tab, tab + 128, 0, 126, A, D, S_dec, threadIdx.x, kRcThreads);
+  if (threadIdx.x < 127) rhoT[threadIdx.x] = encode_reciprocal(e4m3_decode(threadIdx.x), S_dec);
   __syncthreads();
 
   Raw16<InT> nxt;
@@ -259,36 +233,51 @@ __global__ __launch_bounds__(kRcThreads) void k_4over6_2d(
       ab = absmax_bits16(v);
     }
     ab = row16_max(ab);
-    const bool special = ab >= 0x7F800000u;  // uniform over the tile
-    uint32_t c6[2] = {0u, 0u}, c4[2] = {0u, 0u}, k6 = 0, k4 = 0;
-    float E6 = 0.0f, E4 = 0.0f;
-    if (!special) {
-      if (active) {
-        const float sig6 = div_guarded(bits2f(ab), 6.0f, 1.0f / 6.0f) * S_enc;
-        const uint32_t kk = hw_e4m3_pair(fminf(sig6, kE4m3Max), fminf(sig6 * 1.5f, kE4m3Max)) & 0x7F7Fu;
-        k6 = kk & 0xFFu;
-        k4 = kk >> 8;
-        encode16_hw(v, rhoT[k6], c6);
-        encode16_hw(v, rhoT[k4], c4);
-        error_sums<MSE>(v, dT + k6 * kDStride, c6, dT + k4 * kDStride, c4, E6, E4);
-      }
-    } else {
-      // NaN-dropping tile amax, then the software candidates
+    // NaN-dropping tile amax (the integer max of the magnitude bits is the
+    // value max unless the tile holds a NaN)
+    float a = bits2f(ab);
+    if (ab > 0x7F800000u) {
       float l = active ? absmax_nan_drop16(v) : 0.0f;
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) l = fmaxf(l, __shfl_xor(l, off, 64));
-      if (active) {
-        const float sig6 = (l / 6.0f) * S_enc;
-        k6 = e4m3_encode(fminf(sig6, kE4m3Max));
-        k4 = e4m3_encode(fminf(sig6 * 1.5f, kE4m3Max));
-        const float s6 = e4m3_decode(k6), s4 = e4m3_decode(k4);
-        E6 = candidate<MSE>(v, s6, encode_reciprocal(s6, S_dec), A, D, c6[0], c6[1]);
-        E4 = candidate<MSE>(v, s4, encode_reciprocal(s4, S_dec), A, D, c4[0], c4[1]);
-      }
+      a = l;
     }
-    E6 = tree16_sum(E6);
-    E4 = tree16_sum(E4);
-    const bool pick4 = E4 < E6;
+    const float sig6 = div_guarded(a, 6.0f, 1.0f / 6.0f) * S_enc;
+    const uint32_t kk = hw_e4m3_pair(fminf(sig6, kE4m3Max), fminf(sig6 * 1.5f, kE4m3Max)) & 0x7F7Fu;
+    const uint32_t k6 = kk & 0xFFu, k4 = kk >> 8;
+    const float rho6 = rhoT[k6], rho4 = rhoT[k4];
+    const float s6 = e4m3_decode(k6), s4 = e4m3_decode(k4);
+    uint32_t c6[2] = {0u, 0u}, c4[2] = {0u, 0u};
+    float E6 = 0.0f, E4 = 0.0f;
+    if (active) {
+      float v6[16], v4[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        v6[i] = v[i] * rho6;
+        v4[i] = v[i] * rho4;
+      }
+      encode16_hw(v, rho6, c6);
+      encode16_hw(v, rho4, c4);
+      E6 = approx_error16<MSE>(v6, c6);
+      E4 = approx_error16<MSE>(v4, c4);
+    }
+    // the decision is uniform over the tile (every lane holds the same tree totals)
+    int pick = certified_pick<MSE, 8>(tree16_sum(E6), tree16_sum(E4), s6 * S_dec, s4 * S_dec, a);
+    if (pick < 0) {  // exact row errors, then the same tree
+      if (active) {
+        if (pick == -1) {
+          E6 = exact_error16<MSE>(v, c6, s6, A, D);
+          E4 = exact_error16<MSE>(v, c4, s4, A, D);
+        } else {
+          E6 = candidate<MSE>(v, s6, rho6, A, D, c6[0], c6[1]);
+          E4 = candidate<MSE>(v, s4, rho4, A, D, c4[0], c4[1]);
+        }
+      }
+      E6 = tree16_sum(E6);
+      E4 = tree16_sum(E4);
+      pick = E4 < E6 ? 1 : 0;
+    }
+    const bool pick4 = pick == 1;
     const uint32_t c0 = pick4 ? c4[0] : c6[0], c1 = pick4 ? c4[1] : c6[1];
     if (active) {
       *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c0, c1);

@@ -203,6 +203,13 @@ NV_DEV uint32_t hw_e4m3_pair(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// gfx950 e4m3 byte SEL of c -> fp32: equal to e4m3_decode on every code
+// 0x00..0x7E (checked exhaustively).
+template <int SEL>
+NV_DEV float hw_e4m3_value(uint32_t c) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)c, SEL);
+}
+
 // Global scale from amax A and D = 6 * bound: S_enc = min(D / A, FLT_MAX),
 // S_dec = A / D (true divisions).
 NV_DEV void global_scales(float A, float D, float& S_enc, float& S_dec) {

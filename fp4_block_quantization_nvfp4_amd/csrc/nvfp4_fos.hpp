@@ -5,74 +5,16 @@
 //
 // A candidate (map-to-6 or map-to-4) is the block's codes under one e4m3
 // scale s plus its dequantization error, summed in element order 0..15, of
-// d = ((val * s) * A) / D against the input.  With A and D fixed, d depends
-// only on the scale code and the code's magnitude, so kernels keep a table
-// of d (and of the encode reciprocals rho) in LDS and look elements up.
+// d = ((val * s) * A) / D against the input.  Kernels keep the encode
+// reciprocals rho of all 127 scale codes in LDS and decide between the
+// candidates from error sums in the scaled domain whenever a rounding bound
+// proves the decision (certified_pick below); otherwise they compute the
+// exact error sums.
 #pragma once
 
 #include "nvfp4_device.hpp"
 
 namespace nvfp4 {
-
-NV_DEV float e2m1_value(uint32_t m) {
-  return m <= 4u ? (float)m * 0.5f : (m == 5u ? 3.0f : (m == 6u ? 4.0f : 6.0f));
-}
-
-constexpr int kDStride = 9;  // floats per scale code in the d table (8 used; 9 spreads LDS banks)
-constexpr int kTabFloats = 128 + 127 * kDStride;  // rho[128] then d[127][kDStride]
-
-// Fill rho[k] = min(1 / (s_k * S_dec), FLT_MAX) and d[k][m] = ((v_m * s_k) * A) / D
-// for scale codes k in [kmin, kmax], shared by the nthreads lanes of the
-// workgroup (lane `tid`).  The caller synchronizes afterwards.
-NV_DEV void build_fos_tables(float* rhoT, float* dT, int kmin, int kmax, float A, float D,
-                             float S_dec, int tid, int nthreads) {
-  if (kmin > kmax) return;
-  const float rD = 1.0f / D;
-  for (int k = kmin + tid; k <= kmax; k += nthreads)
-    rhoT[k] = encode_reciprocal(e4m3_decode((uint32_t)k), S_dec);
-  const int n = (kmax - kmin + 1) * 8;
-  for (int e = tid; e < n; e += nthreads) {
-    const uint32_t k = (uint32_t)kmin + (uint32_t)(e >> 3);
-    dT[k * kDStride + (e & 7)] = div_guarded((e2m1_value((uint32_t)(e & 7)) * e4m3_decode(k)) * A, D, rD);
-  }
-}
-
-// Error sums of both candidates over a block, each in element order: t6 / t4
-// point at the candidates' rows of the d table, c6 / c4 hold their 16 codes;
-// element i's d is entry (code & 7).  The codes are first spread to one byte
-// per element (4 * (code & 7); even elements from the low nibbles, odd from
-// the high nibbles) so that each LDS address is one add with a byte-select
-// operand; the empty asm keeps the compiler from re-deriving per-element
-// shifts.  All 32 lookups are issued before the sums so the LDS latency of
-// one block overlaps.  |x - d| and (x - d)^2 are unchanged when both signs
-// flip, so the error is taken on magnitudes.
-template <bool MSE>
-NV_DEV void error_sums(const float xv[16], const float* t6, const uint32_t c6[2], const float* t4,
-                       const uint32_t c4[2], float& E6, float& E4) {
-  const char* tb6 = reinterpret_cast<const char*>(t6);
-  const char* tb4 = reinterpret_cast<const char*>(t4);
-  float d6[16], d4[16];
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    uint32_t ev6 = (c6[w] << 2) & 0x1C1C1C1Cu, od6 = (c6[w] >> 2) & 0x1C1C1C1Cu;
-    uint32_t ev4 = (c4[w] << 2) & 0x1C1C1C1Cu, od4 = (c4[w] >> 2) & 0x1C1C1C1Cu;
-    asm("" : "+v"(ev6), "+v"(od6), "+v"(ev4), "+v"(od4));
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      d6[8 * w + 2 * b] = *reinterpret_cast<const float*>(tb6 + ((ev6 >> (8 * b)) & 0xFFu));
-      d6[8 * w + 2 * b + 1] = *reinterpret_cast<const float*>(tb6 + ((od6 >> (8 * b)) & 0xFFu));
-      d4[8 * w + 2 * b] = *reinterpret_cast<const float*>(tb4 + ((ev4 >> (8 * b)) & 0xFFu));
-      d4[8 * w + 2 * b + 1] = *reinterpret_cast<const float*>(tb4 + ((od4 >> (8 * b)) & 0xFFu));
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float u6 = fabsf(xv[i]) - d6[i], u4 = fabsf(xv[i]) - d4[i];
-    const float e6 = MSE ? u6 * u6 : fabsf(u6), e4 = MSE ? u4 * u4 : fabsf(u4);
-    E6 = (i == 0) ? e6 : E6 + e6;
-    E4 = (i == 0) ? e4 : E4 + e4;
-  }
-}
 
 // Codes of one candidate: v = x * rho, rounded to e2m1 by the hardware
 // conversion, two elements per instruction, even element in the low nibble.
@@ -129,6 +71,239 @@ NV_DEV float candidate(const float xv[16], float s, float rho, float A, float D,
     E = (i == 0) ? e : E + e;
   }
   return E;
+}
+
+// ---------------------------------------------------------------------------
+// Certified candidate choice without the per-element dequant values.
+//
+// The exact rule compares E_c = sum_i e_i (in element order, e_i = |x_i - d_i|
+// or (x_i - d_i)^2, d_i = fl(fl(q_i s_c A) / D)) for c = 4 and 6.  Both
+// candidates' codes come from v_i = fl(|x_i| rho_c), rho_c = fl(1 / W_c),
+// W_c = fl(s_c S_dec), S_dec = fl(A / D), so the kernel already holds v_i
+// and (by the exact hardware fp4 -> fp32 conversion) q_i.  Let c = s_c A / D
+// (real), S = sum |x_i| <= N a (N elements, amax a), T = sum ||x_i| - q_i c|,
+// u = 2^-24.  Every d_i carries two roundings (|d_i - q_i c| <= 2.01 u q_i c,
+// and c sum q_i <= S + T), every e_i one more, and the element-order sum
+// 15 u sum e_i (19 u for 16 row sums combined by a depth-4 tree), so
+//   |E_c - T| <= 2.02 u S + 18.1 u T            (1x16; 22.1 u T for tiles).
+// On the approximate side v_i = (|x_i| / c)(1 + eta_i), |eta_i| <= 4.01 u (S_dec,
+// W, rho and the product), and Z_c = fl(W_c E'_c) with E'_c = sum |v_i - q_i|:
+//   |Z_c - T| <= 4.02 u S + 19.1 u T            (1x16; 23.1 u T for tiles).
+// Hence |Z_c - E_c| <= 6.04 u S + 37.2 u T (45.2 u T), and with S <= 16 a
+// (256 a) both candidates together stay below 194 u a + 38 u (Z_4 + Z_6)
+// (3092 u a + 46 u (Z_4 + Z_6) for tiles).  For MSE (E'_c = sum (v_i - q_i)^2,
+// Z_c = W_c^2 E'_c) the same steps with |x_i| |t_i| <= (x_i^2 + t_i^2) / 2
+// give 193 u a^2 + 51 u (Z_4 + Z_6) (3084 u a^2 + 59 u (...) for tiles).  The
+// margin B = k a (or k a^2) + 2^-15 (Z_4 + Z_6) + 2^-90, k = 2^-15 for 1x16
+// and 2^-11 for tiles, covers these at least 2.6 times over (the 2^-90 term
+// covers subnormal products), so
+//   Z_4 + B < Z_6  proves E_4 < E_6 (map-to-4), and
+//   Z_4 - B >= Z_6 proves E_4 >= E_6 (map-to-6, ties included).
+// The range guards (2^-50 <= W_6 <= W_4 <= 2^50, a <= 2^50, finite Z, no
+// NaN) keep every d_i, v_i and partial sum normal and finite.  Undecided
+// blocks (exact ties occur in real data) take exact_error16 below; blocks
+// outside the guards (NaN, infinities, zero or clipped scales) take the
+// software candidate.
+
+// Approximate error sum of one candidate from its scaled values v (signed,
+// x * rho) and its codes c (q_i has the sign of v_i, so |v_i - q_i| is the
+// distance of the magnitudes).
+template <bool MSE>
+NV_DEV float approx_error16(const float v[16], const uint32_t c[2]) {
+  float q[16];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const nv_f2 p0 = hw_fp4_values<0>(c[w]), p1 = hw_fp4_values<1>(c[w]);
+    const nv_f2 p2 = hw_fp4_values<2>(c[w]), p3 = hw_fp4_values<3>(c[w]);
+    q[8 * w + 0] = p0.x; q[8 * w + 1] = p0.y; q[8 * w + 2] = p1.x; q[8 * w + 3] = p1.y;
+    q[8 * w + 4] = p2.x; q[8 * w + 5] = p2.y; q[8 * w + 6] = p3.x; q[8 * w + 7] = p3.y;
+  }
+  float E = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float t = v[i] - q[i];
+    E = MSE ? __builtin_fmaf(t, t, E) : E + fabsf(t);
+  }
+  return E;
+}
+
+// Exact element-order error sum of one candidate with codes c (finite
+// inputs, scale s, inside the range guards).  A code value is q = mu 2^k
+// with mu in {1, 1.5}, so fl(q s A) = 2^k fl(mu s A) and
+// d = fl(fl(q s A) / D) = 2^k fl(fl(mu s A) / D) while everything stays
+// normal: two correctly rounded divisions per candidate instead of one per
+// element.  2^k is q's exponent field (0 for q = 0), mu is its top mantissa
+// bit.
+template <bool MSE>
+NV_DEV float exact_error16(const float xv[16], const uint32_t c[2], float s, float A, float D) {
+  const float rD = 1.0f / D;
+  const float Q1 = div_guarded(s * A, D, rD);
+  const float Q15 = div_guarded((1.5f * s) * A, D, rD);
+  float E = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      nv_f2 p;
+      if (b == 0) p = hw_fp4_values<0>(c[w]);
+      else if (b == 1) p = hw_fp4_values<1>(c[w]);
+      else if (b == 2) p = hw_fp4_values<2>(c[w]);
+      else p = hw_fp4_values<3>(c[w]);
+      const float qv[2] = {p.x, p.y};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = 8 * w + 2 * b + h;
+        const uint32_t qb = f2bits(qv[h]);
+        const float d = bits2f(qb & 0x7F800000u) * ((qb & 0x400000u) ? Q15 : Q1);
+        const float t = fabsf(xv[i]) - d;
+        const float e = MSE ? t * t : fabsf(t);
+        E = (i == 0) ? e : E + e;
+      }
+    }
+  }
+  return E;
+}
+
+// 1: map-to-4 proven, 0: map-to-6 proven, -1: undecided inside the range
+// guards (use exact_error16), -2: outside them (use the software
+// candidate).  kLog2N = 4 for a 1x16 block, 8 for a 16x16 tile (E6a / E4a
+// then the tile totals).
+template <bool MSE, int kLog2N>
+NV_DEV int certified_pick(float E6a, float E4a, float W6, float W4, float a) {
+  if (!(W6 >= 0x1p-50f && W4 <= 0x1p50f && a <= 0x1p50f)) return -2;
+  if (E6a != E6a || E4a != E4a) return -2;  // a NaN in the block
+  const float Z6 = MSE ? (W6 * W6) * E6a : W6 * E6a;
+  const float Z4 = MSE ? (W4 * W4) * E4a : W4 * E4a;
+  if (!(Z6 <= kFltMax && Z4 <= kFltMax)) return -2;
+  constexpr float kA = kLog2N == 4 ? 0x1p-15f : 0x1p-11f;
+  const float B = kA * (MSE ? a * a : a) + 0x1p-15f * (Z4 + Z6) + 0x1p-90f;
+  if (Z4 + B < Z6) return 1;
+  if (Z4 - B >= Z6) return 0;
+  return -1;
+}
+
+// One candidate's codes (hardware encode, finite input) and approximate
+// error sum, pair by pair: scale two elements, encode them into byte SEL,
+// convert the byte back (exact) and accumulate |v - q| (or (v - q)^2), so
+// no per-element array stays live.
+template <bool MSE, int SEL>
+NV_DEV void fos_pair(float x0, float x1, float rho, uint32_t& c, float& E) {
+  const float v0 = x0 * rho, v1 = x1 * rho;
+  c = hw_fp4_pair<SEL>(c, v0, v1);
+  const nv_f2 q = hw_fp4_values<SEL>(c);
+  const float t0 = v0 - q.x, t1 = v1 - q.y;
+  if (MSE) {
+    E = __builtin_fmaf(t0, t0, E);
+    E = __builtin_fmaf(t1, t1, E);
+  } else {
+    E = E + fabsf(t0);
+    E = E + fabsf(t1);
+  }
+}
+
+template <bool MSE>
+NV_DEV void fos_candidate(const float xv[16], float rho, uint32_t c[2], float& E) {
+  c[0] = 0u;
+  c[1] = 0u;
+  E = 0.0f;
+  fos_pair<MSE, 0>(xv[0], xv[1], rho, c[0], E);
+  fos_pair<MSE, 1>(xv[2], xv[3], rho, c[0], E);
+  fos_pair<MSE, 2>(xv[4], xv[5], rho, c[0], E);
+  fos_pair<MSE, 3>(xv[6], xv[7], rho, c[0], E);
+  fos_pair<MSE, 0>(xv[8], xv[9], rho, c[1], E);
+  fos_pair<MSE, 1>(xv[10], xv[11], rho, c[1], E);
+  fos_pair<MSE, 2>(xv[12], xv[13], rho, c[1], E);
+  fos_pair<MSE, 3>(xv[14], xv[15], rho, c[1], E);
+}
+
+// Both candidates of a block: codes and approximate error sums E'_6, E'_4.
+template <bool MSE>
+NV_DEV void fos_candidates(const float xv[16], float rho6, float rho4, uint32_t c6[2],
+                           uint32_t c4[2], float& E6a, float& E4a) {
+  fos_candidate<MSE>(xv, rho6, c6, E6a);
+  fos_candidate<MSE>(xv, rho4, c4, E4a);
+}
+
+// Scale codes of both candidates: byte 0 map-to-6, byte 1 map-to-4 (each
+// sigma capped at 448 first; hardware round-to-nearest-even e4m3).  The
+// 7-bit masks only matter for a negative amax, which is invalid input: they
+// keep table indexes in range.
+NV_DEV uint32_t fos_scale_codes(float sig6) {
+  return hw_e4m3_pair(fminf(sig6, kE4m3Max), fminf(sig6 * 1.5f, kE4m3Max)) & 0x7F7Fu;
+}
+
+// Four-over-six for one 1x16 block of a row or tensor with amax A: scale
+// codes, both candidates by the hardware encode, then the certified choice,
+// the exact sums of exact_error16 for undecided blocks, or the software
+// candidate (software encoder, true divisions) outside the range guards.  a
+// is the block's NaN-dropping amax, rhoT the encode reciprocals of all 127
+// scale codes for S_dec.  Returns the scale byte.
+template <bool MSE>
+NV_DEV uint32_t fos_block(const float xv[16], float a, float S_enc, float S_dec, float A, float D,
+                          const float* rhoT, uint32_t c[2]) {
+  const uint32_t kk = fos_scale_codes(div_guarded(a, 6.0f, 1.0f / 6.0f) * S_enc);
+  const uint32_t k6 = kk & 0xFFu, k4 = kk >> 8;
+  const float rho6 = rhoT[k6], rho4 = rhoT[k4];
+  const float s6 = hw_e4m3_value<0>(kk), s4 = hw_e4m3_value<1>(kk);
+  uint32_t c6[2], c4[2];
+  float E6a, E4a;
+  fos_candidates<MSE>(xv, rho6, rho4, c6, c4, E6a, E4a);
+  int pick = certified_pick<MSE, 4>(E6a, E4a, s6 * S_dec, s4 * S_dec, a);
+  if (pick == -1) {
+    const float E6 = exact_error16<MSE>(xv, c6, s6, A, D);
+    const float E4 = exact_error16<MSE>(xv, c4, s4, A, D);
+    pick = E4 < E6 ? 1 : 0;
+  } else if (pick == -2) {
+    const float E6 = candidate<MSE>(xv, s6, rho6, A, D, c6[0], c6[1]);
+    const float E4 = candidate<MSE>(xv, s4, rho4, A, D, c4[0], c4[1]);
+    pick = E4 < E6 ? 1 : 0;
+  }
+  c[0] = pick ? c4[0] : c6[0];
+  c[1] = pick ? c4[1] : c6[1];
+  return pick ? k4 : k6;
+}
+
+// The same for a block of a row whose amax A is that row's own NaN-dropping
+// amax (so a <= A and sigma6 <= bound), in a row that passed
+// fos_row_in_range.  The range guards then reduce to a per-block flag: a
+// block is "plain" when its bf16 amax pattern ab16 is finite and at least
+// 2^-117 (a / 6 by the fast exact division) and its map-to-6 scale is not
+// zero; other blocks take the general fos_block.
+NV_DEV bool fos_row_in_range(float A, float S_dec) {
+  return A <= 0x1p50f && S_dec >= 0x1p-41f && S_dec <= 0x1p41f;
+}
+
+template <bool MSE>
+NV_DEV uint32_t fos_block_row(const float xv[16], uint32_t ab16, float S_enc, float S_dec, float A,
+                              float D, const float* rhoT, uint32_t c[2]) {
+  const float a = bits2f(ab16 << 16);
+  const uint32_t kk = fos_scale_codes(div_fast(a, 6.0f, 1.0f / 6.0f) * S_enc);
+  const uint32_t k6 = kk & 0xFFu, k4 = kk >> 8;
+  if (ab16 >= 0x7F80u || ab16 < 0x0500u || k6 == 0u) return fos_block<MSE>(xv, a, S_enc, S_dec, A, D, rhoT, c);
+  const float rho6 = rhoT[k6], rho4 = rhoT[k4];
+  const float s6 = hw_e4m3_value<0>(kk), s4 = hw_e4m3_value<1>(kk);
+  uint32_t c6[2], c4[2];
+  float E6a, E4a;
+  fos_candidates<MSE>(xv, rho6, rho4, c6, c4, E6a, E4a);
+  // In range: 2^-50 <= W6 <= W4 <= 2^50, a <= 2^50, every v_i <= 12, so Z is
+  // finite and no guard is needed (see certified_pick).
+  const float W6 = s6 * S_dec, W4 = s4 * S_dec;
+  const float Z6 = (MSE ? W6 * W6 : W6) * E6a;
+  const float Z4 = (MSE ? W4 * W4 : W4) * E4a;
+  const float B = 0x1p-15f * (MSE ? a * a : a) + 0x1p-15f * (Z4 + Z6) + 0x1p-90f;
+  int pick;
+  if (Z4 + B < Z6) {
+    pick = 1;
+  } else if (Z4 - B >= Z6) {
+    pick = 0;
+  } else {
+    const float E6 = exact_error16<MSE>(xv, c6, s6, A, D);
+    const float E4 = exact_error16<MSE>(xv, c4, s4, A, D);
+    pick = E4 < E6 ? 1 : 0;
+  }
+  c[0] = pick ? c4[0] : c6[0];
+  c[1] = pick ? c4[1] : c6[1];
+  return pick ? k4 : k6;
 }
 
 }  // namespace nvfp4

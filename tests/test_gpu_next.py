@@ -142,3 +142,57 @@ def test_empty_next():
     assert pr.shape == (0, 16) and pc.shape == (32, 0) and sc.shape == (32, 0)
     pr, pc, ts = nv.quantize_4over6_2d(x, 1.0)
     assert ts.shape == (0, 2)
+
+
+def lattice_input(seed, M, K, bf16=True):
+    """Blocks whose values sit on small lattices (block scale 2^e * {1, 1.5}
+    times k/16, k = 0..16, random signs), plus constant and all-zero blocks:
+    both four-over-six candidates often represent such blocks equally well,
+    so exact error ties and near ties are common (the cases a choice made
+    from approximate error sums must hand to the exact computation)."""
+    rng = np.random.default_rng(seed)
+    nb = K // 16
+    scale = (2.0 ** rng.integers(-6, 7, (M, nb)) * rng.choice([1.0, 1.5, 1.25], (M, nb))).astype(np.float32)
+    k = rng.integers(0, 17, (M, nb, 16)).astype(np.float32) / np.float32(16)
+    sgn = rng.choice(np.array([-1, 1], np.float32), (M, nb, 16))
+    x = (scale[..., None] * k * sgn).astype(np.float32)
+    kind = rng.random((M, nb))
+    x[kind < 0.05] = 0.0
+    const = (kind >= 0.05) & (kind < 0.1)
+    x[const] = scale[const][:, None]
+    x = x.reshape(M, K)
+    if bf16:
+        import workloads
+        return workloads.bf16_bits(x)
+    return x
+
+
+@pytest.mark.parametrize("shape", [(64, 7168), (48, 512)])
+@pytest.mark.parametrize("err", ["mae", "mse"])
+@pytest.mark.parametrize("bound", [256.0, 448.0])
+def test_four_over_six_ties(shape, err, bound):
+    M, K = shape
+    x = lattice_input(M + K, M, K)
+    xd = to_dev(x)
+    # row-scaled, amax computed in the kernel
+    Ar = oracle.amax(x, mode="row")
+    wp, ws = oracle.quantize_4over6(x, Ar, err_mode=err, bound=bound)
+    p, s, ga = nv.quantize_4over6(xd, None, err_mode=err, e4m3_scale_bound=bound, row_scaled=True)
+    assert_bitwise(to_np(ga), Ar, "row amax")
+    assert_bitwise(to_np(s), ws, "row-scaled scales")
+    assert_bitwise(to_np(p), wp, "row-scaled codes")
+    # per-tensor amax, and a given amax below the true one (scales clip at 448)
+    for A in (oracle.amax(x), np.float32(oracle.amax(x) / 64)):
+        wp, ws = oracle.quantize_4over6(x, A, err_mode=err, bound=bound)
+        p, s, _ = nv.quantize_4over6(xd, _ga(A), err_mode=err, e4m3_scale_bound=bound, row_scaled=False)
+        assert_bitwise(to_np(s), ws, f"tensor scales A={A}")
+        assert_bitwise(to_np(p), wp, f"tensor codes A={A}")
+        wpr, wsr, wpc, wsc = oracle.quantize_rowcol(x, A, four_over_six=True, err_mode=err, bound=bound)
+        got = nv.quantize_rowcol(xd, _ga(A), four_over_six=True, err_mode=err, e4m3_scale_bound=bound)
+        for g, w, what in zip(got, (wpr, wsr, wpc, wsc), ("pr", "sr", "pc", "sc")):
+            assert_bitwise(to_np(g), w, f"rowcol {what} A={A}")
+        wr, wc, wt = oracle.quantize_4over6_2d(x, A, err_mode=err, bound=bound)
+        r, c, t = nv.quantize_4over6_2d(xd, _ga(A), err_mode=err, e4m3_scale_bound=bound)
+        assert_bitwise(to_np(t), wt, f"2d tiles A={A}")
+        assert_bitwise(to_np(r), wr, f"2d rows A={A}")
+        assert_bitwise(to_np(c), wc, f"2d cols A={A}")

@@ -106,10 +106,15 @@ def e2m1_sr_index(v, u16) -> np.ndarray:
 
     fp4-train, Method: for v between two grid points lo <= v < hi the higher
     point is taken with probability equal to the fractional distance
-    f = (v - lo) / (hi - lo).  Here the uniform draw is u = u16 * 2**-16 and
-    the value rounds up iff u < f.  v >= 6 saturates to 6 with no draw.
-    Both subtraction and division are exact in float32: v - lo by Sterbenz
-    (or lo = 0) and hi - lo is a power of two.
+    f = (v - lo) / (hi - lo).  Reading (the card fixes neither the draw nor
+    the comparison): the uniform draw is u = u16 * 2**-16 and the value
+    rounds up iff u < f22, where f22 is f truncated to 22 fractional bits.
+    On [1, 6) f22 == f; below 1 the truncation moves the decision only when
+    u sits within 2**-22 below f, so P(up) stays within 2**-22 of f (the
+    16-bit draw alone already limits it to 2**-16).  v >= 6 saturates to 6
+    with no draw.  Every step is exact in float32: v - lo by Sterbenz (or
+    lo = 0), hi - lo is a power of two, and the truncation is a floor of f
+    scaled by 2**22.
     """
     v = np.asarray(v, dtype=np.float32)
     u16 = np.asarray(u16)
@@ -120,8 +125,9 @@ def e2m1_sr_index(v, u16) -> np.ndarray:
     g_lo = E2M1_GRID[lo]
     g_hi = E2M1_GRID[lo + 1]
     f = (vv - g_lo) / (g_hi - g_lo)
+    f22 = np.floor(f * F32(2.0 ** 22)) * F32(2.0 ** -22)
     u = u16.astype(np.float32) * F32(2.0 ** -16)
-    up = u < f
+    up = u < f22
     idx = lo + up.astype(np.int64)
     return np.where(sat, 7, idx).astype(np.int64)
 

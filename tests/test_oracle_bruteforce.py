@@ -8,6 +8,7 @@ wrong index, a transposed operand, a dropped term or numpy promotion slip in
 the oracle's vectorised code fails here.  Inputs are finite; special values
 are pinned in test_oracle_pins.py.
 """
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -57,7 +58,8 @@ def _code(x: Fraction, neg: bool, rho, u16=None):
     else:
         lo = max(i for i, g in enumerate(E2M1) if g <= v)
         f = (v - E2M1[lo]) / (E2M1[lo + 1] - E2M1[lo])
-        idx = lo + (1 if Fraction(int(u16), 65536) < f else 0)
+        f22 = Fraction(math.floor(f * 2 ** 22), 2 ** 22)  # fraction to 22 bits (the SR reading)
+        idx = lo + (1 if Fraction(int(u16), 65536) < f22 else 0)
     return (8 if neg else 0) | idx, (-E2M1[idx] if neg else E2M1[idx])
 
 

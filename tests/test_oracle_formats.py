@@ -4,6 +4,7 @@ Each check ties the oracle to something other than itself: the grid printed
 on the fp4-train card, torch's float8_e4m3fn / bfloat16 casts (library
 routines), exact rational enumeration, and byte values the e4m3 format fixes.
 """
+import math
 import os
 from fractions import Fraction
 
@@ -122,9 +123,34 @@ def test_e2m1_sr_fraction_is_exact_and_brackets():
                 assert ii == lo  # on-grid values never move
                 continue
             f = (x - E2M1[lo]) / (E2M1[lo + 1] - E2M1[lo])
-            assert ii == (lo + 1 if Fraction(u16, 65536) < f else lo)
+            f22 = Fraction(math.floor(f * 2 ** 22), 2 ** 22)
+            assert ii == (lo + 1 if Fraction(u16, 65536) < f22 else lo)
     sat = oracle.e2m1_sr_index(np.array([6.0, 7.0, np.inf], np.float32), np.zeros(3))
     assert list(sat) == [7, 7, 7]
+
+
+def test_e2m1_sr_22_bit_fraction_boundaries():
+    # Above 1 the fraction has exactly 22 bits, so the reading changes nothing
+    # there; below 1 a draw just under the exact fraction but not under its
+    # 22-bit truncation keeps the lower grid point.
+    v = np.array([0x3F378F81], np.uint32).view(np.float32)  # 0.717..., odd last mantissa bit
+    f = (exact(v[0]) - Fraction(1, 2)) / Fraction(1, 2)
+    u = math.floor(f * 2 ** 16)
+    assert Fraction(u, 2 ** 16) < f and Fraction(u, 2 ** 16) == Fraction(math.floor(f * 2 ** 22), 2 ** 22)
+    assert oracle.e2m1_sr_index(v, np.array([u]))[0] == 1          # stays at 0.5
+    assert oracle.e2m1_sr_index(v, np.array([u - 1]))[0] == 2      # rounds up to 1.0
+    tiny = np.array([1e-10, 2.0 ** -24, 2.0 ** -23, 3 * 2.0 ** -25], np.float32)
+    assert list(oracle.e2m1_sr_index(tiny, np.zeros(4))) == [0, 0, 1, 0]
+    # on [1, 6) every fraction is representable in 22 bits: same as the exact rule
+    rng = np.random.default_rng(2)
+    w = rng.uniform(1, 6, 5000).astype(np.float32)
+    uu = rng.integers(0, 65536, 5000)
+    for vi, ui, ii in zip(w[:500], uu[:500], oracle.e2m1_sr_index(w, uu)[:500]):
+        x = exact(vi)
+        lo = max(i for i, g in enumerate(E2M1) if g <= x)
+        f = (x - E2M1[lo]) / (E2M1[lo + 1] - E2M1[lo])
+        assert f * 2 ** 22 == math.floor(f * 2 ** 22)
+        assert ii == (lo + 1 if Fraction(int(ui), 65536) < f else lo)
 
 
 def test_bf16_rne_matches_torch():

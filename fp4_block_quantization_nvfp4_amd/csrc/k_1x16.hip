@@ -17,8 +17,8 @@
 // 2 B per lane).  The block amax is reduced across the four lanes with two
 // DPP quad permutations.  Round-to-nearest codes come from the hardware
 // fp32 -> e2m1 conversion and the dequantized values from the exact e2m1 ->
-// fp32 conversion; stochastic rounding is done on the bit patterns and its
-// on-grid results encoded by the same conversion; blocks holding a NaN or an
+// fp32 conversion; stochastic rounding uses the hardware stochastic-rounding
+// conversion with one 16-bit draw per element; blocks holding a NaN or an
 // infinity use the software encoder.  The work is HBM streaming: no LDS, no
 // MFMA.
 #include "nvfp4_device.hpp"
@@ -110,20 +110,19 @@ __global__ __launch_bounds__(kThreads) void k_quant1x16(
   uint32_t codes;
   float xh[4];
   if (SR && !special) {
-    // stochastic rounding on the bit patterns; the signed on-grid results are
-    // encoded exactly by the hardware conversion
+    // stochastic rounding by the hardware conversion, one draw per element
     const uint32_t p0 = (uint32_t)(g * 2);
-    const uint32_t w0 = pcg_hash(p0 ^ key), w1 = pcg_hash((p0 + 1u) ^ key);
-    const uint32_t u7[4] = {(w0 << 7) & 0x7FFF80u, (w0 >> 9) & 0x7FFF80u, (w1 << 7) & 0x7FFF80u,
-                            (w1 >> 9) & 0x7FFF80u};
-    float rv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rv[i] = bits2f(f2bits(e2m1_sr_bits(fabsf(xv[i]) * rho, u7[i])) | (f2bits(xv[i]) & 0x80000000u));
-    codes = hw_fp4_pair<0>(0u, rv[0], rv[1]);
-    codes = hw_fp4_pair<1>(codes, rv[2], rv[3]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xh[i] = (rv[i] * s) * S_dec;
+    const uint32_t t0 = hw_fp4_sr_pair<0>(xv[0] * rho, xv[1] * rho, ~pcg_hash(p0 ^ key));
+    const uint32_t t1 = hw_fp4_sr_pair<1>(xv[2] * rho, xv[3] * rho, ~pcg_hash((p0 + 1u) ^ key));
+    codes = (t0 & 0xFFu) | (t1 & 0xFF00u);
+    if (OUT != 0 || HAS_RES) {
+      const nv_f2 q01 = hw_fp4_values<0>(codes);
+      const nv_f2 q23 = hw_fp4_values<1>(codes);
+      xh[0] = (q01.x * s) * S_dec;
+      xh[1] = (q01.y * s) * S_dec;
+      xh[2] = (q23.x * s) * S_dec;
+      xh[3] = (q23.y * s) * S_dec;
+    }
   } else if (!SR && !special) {
     codes = hw_fp4_pair<0>(0u, xv[0] * rho, xv[1] * rho);
     codes = hw_fp4_pair<1>(codes, xv[2] * rho, xv[3] * rho);

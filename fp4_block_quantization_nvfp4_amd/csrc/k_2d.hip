@@ -11,13 +11,14 @@
 // holds row r of tile t: 16 consecutive elements read with 128-bit loads, so
 // each wave reads 16 rows x 128 contiguous bytes.  The tile amax is reduced
 // across the 16 lanes of the tile with cross-lane max (all 16 lanes of a tile
-// sit in one 16-lane row of the wave; DPP, no LDS).  Round-to-nearest codes
-// come from the hardware fp32 -> e2m1 conversion (exact for finite inputs;
-// tiles holding a NaN or an infinity and stochastic rounding use the
-// software encoder) and the scale byte from the exact fp32 -> e4m3
-// conversion.  The rowwise codes go out as one 8-byte store per lane.  For the columnwise codes each lane stages its 16 codes as
-// bytes in LDS; lane (t, c) then gathers column c of its tile and stores the
-// 16 codes of that column (8 bytes) into row k of packed_col.
+// sit in one 16-lane row of the wave; DPP, no LDS).  Codes come from the
+// hardware fp32 -> e2m1 conversions: round-to-nearest (exact for finite
+// inputs) or stochastic rounding with one 16-bit draw per element; tiles
+// holding a NaN or an infinity use the software encoder.  The scale byte
+// comes from the exact fp32 -> e4m3 conversion.  The rowwise codes go out as
+// one 8-byte store per lane.  For the columnwise codes each lane stages its
+// 16 codes as bytes in LDS; lane (t, c) then gathers column c of its tile
+// into a per-column buffer that is written out once per workgroup.
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 
@@ -118,26 +119,13 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
       }
       const float rho = encode_reciprocal(s, S_dec);
       if (SR && !special) {
-        // stochastic rounding on the bit patterns, then the hardware
-        // conversion encodes the (on-grid, signed) results exactly
+        // stochastic rounding by the hardware conversion, one draw per element
         const uint32_t p0 = (uint32_t)((row * K + col0) >> 1);
-        float rv[16];
+        uint32_t nw[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t w = pcg_hash((p0 + j) ^ key);
-          const float r0 = e2m1_sr_bits(fabsf(xv[2 * j]) * rho, (w << 7) & 0x7FFF80u);
-          const float r1 = e2m1_sr_bits(fabsf(xv[2 * j + 1]) * rho, (w >> 9) & 0x7FFF80u);
-          rv[2 * j] = bits2f(f2bits(r0) | (f2bits(xv[2 * j]) & 0x80000000u));
-          rv[2 * j + 1] = bits2f(f2bits(r1) | (f2bits(xv[2 * j + 1]) & 0x80000000u));
-        }
-        c0 = hw_fp4_pair<0>(c0, rv[0], rv[1]);
-        c0 = hw_fp4_pair<1>(c0, rv[2], rv[3]);
-        c0 = hw_fp4_pair<2>(c0, rv[4], rv[5]);
-        c0 = hw_fp4_pair<3>(c0, rv[6], rv[7]);
-        c1 = hw_fp4_pair<0>(c1, rv[8], rv[9]);
-        c1 = hw_fp4_pair<1>(c1, rv[10], rv[11]);
-        c1 = hw_fp4_pair<2>(c1, rv[12], rv[13]);
-        c1 = hw_fp4_pair<3>(c1, rv[14], rv[15]);
+        for (int j = 0; j < 8; ++j) nw[j] = ~pcg_hash((p0 + j) ^ key);
+        c0 = hw_fp4_sr_word(xv, rho, nw);
+        c1 = hw_fp4_sr_word(xv + 8, rho, nw + 4);
       } else if (!SR && !special) {
         c0 = hw_fp4_pair<0>(c0, xv[0] * rho, xv[1] * rho);
         c0 = hw_fp4_pair<1>(c0, xv[2] * rho, xv[3] * rho);

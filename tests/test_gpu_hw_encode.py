@@ -11,7 +11,13 @@ CPU oracle:
   in [0, 8) whose low 6 mantissa bits are zero, +-2^12 ulps around every
   rounding midpoint, and both signs;
 * scale bytes: one block per amax value, over every positive finite bf16
-  value up to 2688 (sigma = a / 6 up to 448) and 2^20 float32 values.
+  value up to 2688 (sigma = a / 6 up to 448) and 2^20 float32 values;
+* stochastic rounding (the hardware stochastic-rounding conversion with one
+  16-bit draw per element): unit-scale blocks holding values across every
+  binade below 6 (fp32 subnormals included), values just around every grid
+  point, and values whose fraction ends below the 22nd bit, each under
+  several (seed, step) streams, so that many draws land on the truncation
+  boundary; codes, residuals and dequantized values are compared.
 """
 import numpy as np
 import pytest
@@ -70,3 +76,34 @@ def test_e4m3_scale_dense_sweep():
             p, s = nv.quantize(to_dev(xin))
             assert_bitwise(to_np(s), ws, f"scales {dt}")
             assert_bitwise(to_np(p), wp, f"codes {dt}")
+
+
+def test_stochastic_rounding_dense_sweep():
+    rng = np.random.default_rng(4)
+    n = 1 << 19
+    ex = rng.integers(0, 130, n).astype(np.uint32)           # binades 2^-126 .. 2^2, and subnormals
+    v = ((ex << 23) | rng.integers(0, 1 << 23, n, dtype=np.uint32)).view(np.float32)
+    v = v[v < 6.0]
+    grid = np.array([0.5, 1.0, 1.5, 2.0, 3.0, 4.0], np.float32).view(np.uint32)
+    near = (grid[:, None].astype(np.int64) + np.arange(-512, 513)[None, :]).reshape(-1).astype(np.uint32)
+    v = np.concatenate([v, near.view(np.float32), np.array([0.0, 6.0, 7.0, np.inf], np.float32)])
+    v = np.where(rng.random(v.shape) < 0.5, -v, v).astype(np.float32)
+    x = _unit_scale_blocks(v)
+    xd = to_dev(x)
+    for seed, step in ((0, 0), (7, 123), (0xDEADBEEF, 0xFFFFFFFF)):
+        wp, ws = oracle.quantize(x, stochastic=True, seed=seed, step=step)
+        p, s = nv.quantize(xd, stochastic=True, seed=seed, step=step)
+        assert_bitwise(to_np(s), ws, f"scales seed={seed}")
+        assert_bitwise(to_np(p), wp, f"codes seed={seed}")
+        r = np.zeros_like(x)
+        wo = oracle.qdq(x, stochastic=True, residual=r, seed=seed, step=step, out="f32")[0]
+        rd = torch.zeros_like(xd)
+        got = nv.qdq(xd, stochastic=True, residual=rd, seed=seed, step=step, out_dtype=torch.float32)
+        assert_bitwise(to_np(got), wo, f"qdq seed={seed}")
+        assert_bitwise(to_np(rd), r, f"residual seed={seed}")
+    x2 = np.ascontiguousarray(x[: x.shape[0] // 16 * 16])
+    wr, wc, wt = oracle.quantize_2d(x2, stochastic=True, seed=3, step=4)
+    r2, c2, t2 = nv.quantize_2d(to_dev(x2), stochastic=True, seed=3, step=4)
+    assert_bitwise(to_np(t2), wt, "2d tile scales")
+    assert_bitwise(to_np(r2), wr, "2d rowwise")
+    assert_bitwise(to_np(c2), wc, "2d columnwise")

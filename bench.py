@@ -38,7 +38,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_4over6_act_rows_8192x7168
 
 def src_hash(path=KERNEL_SRC):
     h = hashlib.sha256()
-    for p in (path, os.path.join(os.path.dirname(path), "nvfp4_device.hpp")):
+    d = os.path.dirname(path)
+    for p in (path, os.path.join(d, "nvfp4_device.hpp"), os.path.join(d, "nvfp4_fos.hpp")):
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -255,8 +256,9 @@ def main():
 
 def extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle, steps, warmup):
     """Time the other quantization workloads (GPU only), each parity-checked
-    on a sample first; kernel durations from event pairs around each launch.
-    Returns {name: {...}}."""
+    on a sample first; time per call over the whole timed region (kernel
+    durations of the same runs are in the committed all-workload kernel
+    trace).  Returns {name: {...}}."""
     out = {}
 
     def rec(name, ms, algo, note):
@@ -271,13 +273,13 @@ def extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle, steps, war
     s = torch.empty((256, 16), dtype=torch.uint8, device="cuda")
     o = torch.empty((256, 256), dtype=torch.bfloat16, device="cuda")
     for sr in (0, 1):
-        ms = time_each_ms(torch, lambda i: lib.nvfp4_quantize(xd.data_ptr(), L.F32, 256, 256, None, None, sr, 0, 0,
+        ms = time_ms(torch, lambda i: lib.nvfp4_quantize(xd.data_ptr(), L.F32, 256, 256, None, None, sr, 0, 0,
                                                           p.data_ptr(), s.data_ptr(), stream), warmup, steps)
         wp, ws = oracle.quantize(x, stochastic=bool(sr))
         check_rows(np, p.cpu().numpy(), wp, "small codes")
         rec(f"small_256x256_fp32_quantize_{'sr' if sr else 'rtn'}", ms, 256 * 256 * 4 + 256 * 128 + 256 * 16,
             "launch-bound")
-    ms = time_each_ms(torch, lambda i: lib.nvfp4_dequantize(p.data_ptr(), s.data_ptr(), 256, 256, 0, None, 0, 448.0,
+    ms = time_ms(torch, lambda i: lib.nvfp4_dequantize(p.data_ptr(), s.data_ptr(), 256, 256, 0, None, 0, 448.0,
                                                         o.data_ptr(), L.BF16, stream), warmup, steps)
     rec("small_256x256_dequantize_bf16", ms, 256 * 128 + 256 * 16 + 256 * 256 * 2, "launch-bound")
 
@@ -288,7 +290,7 @@ def extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle, steps, war
     rs = [torch.zeros_like(w) for _ in range(N_SETS)]
     outs = [torch.empty((Mw, Kw), dtype=torch.bfloat16, device="cuda") for _ in range(N_SETS)]
     for sr in (0, 1):
-        ms = time_each_ms(torch, lambda i: lib.nvfp4_qdq(xs[i % N_SETS].data_ptr(), L.F32, Mw, Kw, rs[i % N_SETS].data_ptr(),
+        ms = time_ms(torch, lambda i: lib.nvfp4_qdq(xs[i % N_SETS].data_ptr(), L.F32, Mw, Kw, rs[i % N_SETS].data_ptr(),
                                                      None, sr, 0, i, outs[i % N_SETS].data_ptr(), L.BF16, None, None,
                                                      stream), warmup, steps)
         rec(f"ef_weight_4096x4096_qdq_step_{'sr' if sr else 'rtn'}_ef", ms, Mw * Kw * 14,
@@ -305,9 +307,9 @@ def extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle, steps, war
     pc = [torch.empty((Kt, Mt // 2), dtype=torch.uint8, device="cuda") for _ in range(2)]
     ts = [torch.empty((Mt // 16, Kt // 16), dtype=torch.uint8, device="cuda") for _ in range(2)]
     lib.nvfp4_amax(wd[0].data_ptr(), L.BF16, Mt, Kt, None, L.SCALE_TENSOR, ga.data_ptr(), wsb.data_ptr(), wsz, stream)
-    ms_amax = time_each_ms(torch, lambda i: lib.nvfp4_amax(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, None, L.SCALE_TENSOR,
+    ms_amax = time_ms(torch, lambda i: lib.nvfp4_amax(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, None, L.SCALE_TENSOR,
                                                        ga.data_ptr(), wsb.data_ptr(), wsz, stream), warmup, steps)
-    ms_2d = time_each_ms(torch, lambda i: lib.nvfp4_quantize_2d(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(), 1, 0, 0, 0,
+    ms_2d = time_ms(torch, lambda i: lib.nvfp4_quantize_2d(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(), 1, 0, 0, 0,
                                                             pr[i % 2].data_ptr(), pc[i % 2].data_ptr(),
                                                             ts[i % 2].data_ptr(), stream), warmup, steps)
     A = oracle.amax(wb)
@@ -320,12 +322,12 @@ def extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle, steps, war
     n2 = Mt * Kt
     rec("weight_2d_7168x18432_quantize_2d_sr", ms_2d, n2 * 2 + n2 // 2 + n2 // 2 + n2 // 256,
         "fused pass: bf16 in, rowwise + columnwise codes, tile scales")
-    ms_tf = time_each_ms(torch, lambda i: lib.nvfp4_quantize_2d(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(), 1, 0, 0, 1,
+    ms_tf = time_ms(torch, lambda i: lib.nvfp4_quantize_2d(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(), 1, 0, 0, 1,
                                                             pr[i % 2].data_ptr(), pc[i % 2].data_ptr(),
                                                             ts[i % 2].data_ptr(), stream), warmup, steps)
     rec("weight_2d_7168x18432_quantize_2d_sr_truncation_free", ms_tf, n2 * 2 + n2 // 2 + n2 // 2 + n2 // 256,
         "as above, tile scale rounded up")
-    ms_46 = time_each_ms(torch, lambda i: lib.nvfp4_quantize_4over6_2d(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(),
+    ms_46 = time_ms(torch, lambda i: lib.nvfp4_quantize_4over6_2d(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(),
                                                                    L.MAE, 256.0, pr[i % 2].data_ptr(),
                                                                    pc[i % 2].data_ptr(), ts[i % 2].data_ptr(),
                                                                    stream), warmup, steps)
@@ -338,7 +340,7 @@ def extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle, steps, war
     scol = torch.empty((Kt, Mt // 16), dtype=torch.uint8, device="cuda")
     for fos in (0, 1):
         bnd = 256.0 if fos else 448.0
-        ms_rc = time_each_ms(torch, lambda i: lib.nvfp4_quantize_rowcol(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(),
+        ms_rc = time_ms(torch, lambda i: lib.nvfp4_quantize_rowcol(wd[i % 2].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(),
                                                                     fos, L.MAE, bnd, pr[i % 2].data_ptr(),
                                                                     srow.data_ptr(), pc[i % 2].data_ptr(),
                                                                     scol.data_ptr(), stream), warmup, steps)
@@ -363,7 +365,7 @@ def extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle, steps, war
     wo = oracle.qdq(hb[:64], stochastic=True, residual=rr, seed=7, step=123)[0]
     check_rows(np, ho[:64].cpu().view(torch.int16).numpy().view(np.uint16), wo, "heavy qdq out")
     check_rows(np, r0[:64].cpu().numpy(), rr, "heavy residual")
-    ms = time_each_ms(torch, lambda i: lib.nvfp4_qdq(hd.data_ptr(), L.BF16, Mh, Kh, r0.data_ptr(), None, 1, 7, 123,
+    ms = time_ms(torch, lambda i: lib.nvfp4_qdq(hd.data_ptr(), L.BF16, Mh, Kh, r0.data_ptr(), None, 1, 7, 123,
                                                  ho.data_ptr(), L.BF16, None, None, stream), warmup, steps)
     rec("heavy_16384x8192_qdq_sr_ef", ms, Mh * Kh * 12, "bf16 in, fp32 residual in/out, bf16 out")
     return out

@@ -5,8 +5,8 @@
 // one pass (the fused row + column kernel the four-over-six pull request lists
 // as a follow-up), so no caller-side transpose is needed.
 //
-// Mapping: a workgroup of 256 lanes covers 256 columns and walks down up to
-// 16 strips of 16 rows (a 256 x 256 region); in each strip it holds 16 tiles
+// Mapping: a workgroup of 512 lanes covers 512 columns and walks down up to
+// 16 strips of 16 rows (a 256 x 512 region); in each strip it holds 32 tiles
 // side by side, four per wave.  Lane (t, r) = (tid / 16, tid % 16)
 // holds row r of tile t: 16 consecutive elements read with 128-bit loads, so
 // each wave reads 16 rows x 128 contiguous bytes.  The tile amax is reduced
@@ -24,7 +24,8 @@
 
 namespace nvfp4 {
 
-constexpr int k2dThreads = 256;
+constexpr int k2dThreads = 512;            // lanes per workgroup = columns covered (16 per tile)
+constexpr int k2dTiles = k2dThreads / 16;   // tiles side by side
 
 // Max over the 16 lanes of a DPP row (every lane of the row gets it): two
 // quad permutations, then the half-row and row mirrors.
@@ -47,11 +48,11 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     const InT* __restrict__ x, const float* __restrict__ global_amax, uint32_t key, int64_t M,
     int64_t K, uint8_t* __restrict__ packed_row, uint8_t* __restrict__ packed_col,
     uint8_t* __restrict__ tile_scales, int64_t ncolg) {
-  __shared__ uint4 stage[16 * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (bank spread)
-  __shared__ uint2 colbuf[COL ? 256 * kColStride : 1];
+  __shared__ uint4 stage[k2dTiles * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (bank spread)
+  __shared__ uint2 colbuf[COL ? k2dThreads * kColStride : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
   const int64_t sg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - sg * ncolg;
-  const int64_t col0 = cg * 256 + 16 * t;
+  const int64_t col0 = cg * k2dThreads + 16 * t;
   const bool active = col0 < K;  // uniform over the 16 lanes of a tile
   const int64_t nstrips_total = M / 16;
   const int nst = (int)((nstrips_total - sg * kStrips) < kStrips ? (nstrips_total - sg * kStrips) : kStrips);
@@ -190,8 +191,8 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     // packed_col row; 16 lanes write one column (8 bytes each), so every
     // store instruction covers four whole column segments.
     const int q = threadIdx.x & 15;
-    for (int cc = threadIdx.x >> 4; cc < 256; cc += k2dThreads / 16) {
-      const int64_t col = cg * 256 + cc;
+    for (int cc = threadIdx.x >> 4; cc < k2dThreads; cc += k2dThreads / 16) {
+      const int64_t col = cg * k2dThreads + cc;
       if (col < K && q < nst)
         *reinterpret_cast<uint2*>(packed_col + col * (M / 2) + sg * (kStrips * 8) + q * 8) =
             colbuf[cc * kColStride + q];
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
 template <typename InT, bool SR, bool GLOBAL, bool UP>
 static int launch2d_col(const InT* x, const float* ga, uint32_t key, int64_t M, int64_t K,
                         uint8_t* pr, uint8_t* pc, uint8_t* ts, hipStream_t st) {
-  const int64_t ncolg = (K + 255) / 256;
+  const int64_t ncolg = (K + k2dThreads - 1) / k2dThreads;
   const int64_t nsg = (M / 16 + kStrips - 1) / kStrips;
   const dim3 grid((unsigned)(ncolg * nsg)), block(k2dThreads);
   if (pc) hipLaunchKernelGGL((k_quant2d<InT, SR, GLOBAL, true, UP>), grid, block, 0, st, x, ga, key, M, K, pr, pc, ts, ncolg);

@@ -15,9 +15,10 @@
 //    exact width-16 tree of the pull request's CuTe DSL kernel Design, and
 //    map-to-4 is kept iff its tile error is strictly lower.
 //
-// Mapping (both): a workgroup of 256 lanes covers 256 columns and walks down
-// up to kStripsRC strips of 16 rows.  In a strip it holds 16 tiles side by
-// side, four per wave; lane (t, r) = (tid / 16, tid % 16) reads row r of tile
+// Mapping (both): a workgroup of NT lanes covers NT columns and walks down
+// up to STR strips of 16 rows (256 x 8 for k_rowcol, 512 x 16 for
+// k_4over6_2d).  In a strip it holds NT / 16 tiles side by side, four per
+// wave; lane (t, r) = (tid / 16, tid % 16) reads row r of tile
 // t (16 consecutive elements, 128-bit loads) and the next strip's row is
 // loaded while the current one is encoded.  Columnwise blocks are formed in
 // LDS: k_rowcol stages the tile's values (lane (t, c) then reads column c of
@@ -35,9 +36,9 @@
 
 namespace nvfp4 {
 
-constexpr int kRcThreads = 256;
-constexpr int kStripsRC = 8;                  // 16-row strips per workgroup
-constexpr int kColStrideRC = kStripsRC + 1;   // per-column slots in the column buffers (+1: banks)
+// Workgroup shapes (lanes = columns covered, 16-row strips per workgroup).
+constexpr int kRowColThreads = 256, kRowColStrips = 8;
+constexpr int k46TileThreads = 512, k46TileStrips = 16;
 constexpr int kXRow = 20;                     // floats per staged row (16 used; 80 B keeps 16 B alignment)
 constexpr int kXTile = 16 * kXRow + 16;       // floats per staged tile (+16 shifts tiles across banks)
 
@@ -124,34 +125,35 @@ struct Raw16 {
 // Write the column buffers of a workgroup: column cc of the workgroup owns
 // nst * 8 contiguous code bytes of its packed_col row (and nst scale bytes of
 // its scales_col row); 16 lanes serve one column.
+template <int NT, int STR>
 NV_DEV void flush_columns(const uint2* colbuf, const uint8_t* csbuf, int64_t cg, int64_t sg, int nst,
                           int64_t M, int64_t K, uint8_t* packed_col, uint8_t* scales_col) {
   const int q = threadIdx.x & 15;
-  for (int cc = threadIdx.x >> 4; cc < 256; cc += kRcThreads / 16) {
-    const int64_t col = cg * 256 + cc;
+  for (int cc = threadIdx.x >> 4; cc < NT; cc += NT / 16) {
+    const int64_t col = cg * NT + cc;
     if (col < K && q < nst) {
-      const int64_t strip = sg * kStripsRC + q;
-      *reinterpret_cast<uint2*>(packed_col + col * (M / 2) + strip * 8) = colbuf[cc * kColStrideRC + q];
-      if (scales_col) scales_col[col * (M / 16) + strip] = csbuf[cc * kColStrideRC + q];
+      const int64_t strip = sg * STR + q;
+      *reinterpret_cast<uint2*>(packed_col + col * (M / 2) + strip * 8) = colbuf[cc * (STR + 1) + q];
+      if (scales_col) scales_col[col * (M / 16) + strip] = csbuf[cc * (STR + 1) + q];
     }
   }
 }
 
-template <typename InT, bool FOS, bool MSE>
-__global__ __launch_bounds__(kRcThreads) void k_rowcol(
+template <typename InT, bool FOS, bool MSE, int NT, int STR>
+__global__ __launch_bounds__(NT) void k_rowcol(
     const InT* __restrict__ x, const float* __restrict__ global_amax, float D, int64_t M, int64_t K,
     uint8_t* __restrict__ packed_row, uint8_t* __restrict__ scales_row,
     uint8_t* __restrict__ packed_col, uint8_t* __restrict__ scales_col, int64_t ncolg) {
-  __shared__ __attribute__((aligned(16))) float xs[16 * kXTile];
-  __shared__ uint2 colbuf[256 * kColStrideRC];
-  __shared__ uint8_t csbuf[256 * kColStrideRC];
+  __shared__ __attribute__((aligned(16))) float xs[(NT / 16) * kXTile];
+  __shared__ uint2 colbuf[NT * (STR + 1)];
+  __shared__ uint8_t csbuf[NT * (STR + 1)];
   __shared__ float rhoT[FOS ? 128 : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
   const int64_t sg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - sg * ncolg;
-  const int64_t col0 = cg * 256 + 16 * t;
+  const int64_t col0 = cg * NT + 16 * t;
   const bool active = col0 < K;  // uniform over the 16 lanes of a tile
   const int64_t nstrips = M / 16;
-  const int nst = (int)((nstrips - sg * kStripsRC) < kStripsRC ? (nstrips - sg * kStripsRC) : kStripsRC);
+  const int nst = (int)((nstrips - sg * STR) < STR ? (nstrips - sg * STR) : STR);
 
   const float A = global_amax[0];
   float S_enc, S_dec;
@@ -164,9 +166,9 @@ __global__ __launch_bounds__(kRcThreads) void k_rowcol(
   float* stage = xs + t * kXTile;
 
   Raw16<InT> nxt;
-  if (active) nxt.load(x + (sg * kStripsRC * 16 + r) * K + col0);
+  if (active) nxt.load(x + (sg * STR * 16 + r) * K + col0);
   for (int st = 0; st < nst; ++st) {
-    const int64_t row = (sg * kStripsRC + st) * 16 + r;
+    const int64_t row = (sg * STR + st) * 16 + r;
     const Raw16<InT> cur = nxt;
     if (active && st + 1 < nst) nxt.load(x + (row + 16) * K + col0);
     if (active) {
@@ -190,28 +192,28 @@ __global__ __launch_bounds__(kRcThreads) void k_rowcol(
       uint32_t c[2];
       const uint32_t sc = FOS ? block_fos<MSE>(v, S_enc, S_dec, A, D, rhoT, c)
                               : block_standard(v, mul, S_dec, c);
-      colbuf[(16 * t + r) * kColStrideRC + st] = make_uint2(c[0], c[1]);
-      csbuf[(16 * t + r) * kColStrideRC + st] = (uint8_t)sc;
+      colbuf[(16 * t + r) * (STR + 1) + st] = make_uint2(c[0], c[1]);
+      csbuf[(16 * t + r) * (STR + 1) + st] = (uint8_t)sc;
     }
     __syncthreads();
   }
-  flush_columns(colbuf, csbuf, cg, sg, nst, M, K, packed_col, scales_col);
+  flush_columns<NT, STR>(colbuf, csbuf, cg, sg, nst, M, K, packed_col, scales_col);
 }
 
-template <typename InT, bool MSE, bool COL>
-__global__ __launch_bounds__(kRcThreads) void k_4over6_2d(
+template <typename InT, bool MSE, bool COL, int NT, int STR>
+__global__ __launch_bounds__(NT) void k_4over6_2d(
     const InT* __restrict__ x, const float* __restrict__ global_amax, float D, int64_t M, int64_t K,
     uint8_t* __restrict__ packed_row, uint8_t* __restrict__ packed_col,
     uint8_t* __restrict__ tile_scales, int64_t ncolg) {
   __shared__ float rhoT[128];
-  __shared__ uint4 stage[16 * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (banks)
-  __shared__ uint2 colbuf[COL ? 256 * kColStrideRC : 1];
+  __shared__ uint4 stage[(NT / 16) * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (banks)
+  __shared__ uint2 colbuf[COL ? NT * (STR + 1) : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
   const int64_t sg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - sg * ncolg;
-  const int64_t col0 = cg * 256 + 16 * t;
+  const int64_t col0 = cg * NT + 16 * t;
   const bool active = col0 < K;
   const int64_t nstrips = M / 16;
-  const int nst = (int)((nstrips - sg * kStripsRC) < kStripsRC ? (nstrips - sg * kStripsRC) : kStripsRC);
+  const int nst = (int)((nstrips - sg * STR) < STR ? (nstrips - sg * STR) : STR);
 
   const float A = global_amax[0];
   float S_enc, S_dec;
@@ -220,9 +222,9 @@ __global__ __launch_bounds__(kRcThreads) void k_4over6_2d(
   __syncthreads();
 
   Raw16<InT> nxt;
-  if (active) nxt.load(x + (sg * kStripsRC * 16 + r) * K + col0);
+  if (active) nxt.load(x + (sg * STR * 16 + r) * K + col0);
   for (int st = 0; st < nst; ++st) {
-    const int64_t row0 = (sg * kStripsRC + st) * 16;
+    const int64_t row0 = (sg * STR + st) * 16;
     const int64_t row = row0 + r;
     const Raw16<InT> cur = nxt;
     if (active && st + 1 < nst) nxt.load(x + (row + 16) * K + col0);
@@ -301,17 +303,18 @@ __global__ __launch_bounds__(kRcThreads) void k_4over6_2d(
           if (rr < 8) o0 |= code << (4 * rr);
           else o1 |= code << (4 * (rr - 8));
         }
-        colbuf[(16 * t + r) * kColStrideRC + st] = make_uint2(o0, o1);
+        colbuf[(16 * t + r) * (STR + 1) + st] = make_uint2(o0, o1);
       }
       __syncthreads();
     }
   }
-  if (COL) flush_columns(colbuf, nullptr, cg, sg, nst, M, K, packed_col, nullptr);
+  if (COL) flush_columns<NT, STR>(colbuf, nullptr, cg, sg, nst, M, K, packed_col, nullptr);
 }
 
+template <int NT, int STR>
 static dim3 rc_grid(int64_t M, int64_t K, int64_t& ncolg) {
-  ncolg = (K + 255) / 256;
-  const int64_t nsg = (M / 16 + kStripsRC - 1) / kStripsRC;
+  ncolg = (K + NT - 1) / NT;
+  const int64_t nsg = (M / 16 + STR - 1) / STR;
   return dim3((unsigned)(ncolg * nsg));
 }
 
@@ -319,14 +322,15 @@ template <typename InT>
 static int launch_rowcol_t(const InT* x, const float* ga, int fos, int mse, float D, int64_t M,
                            int64_t K, uint8_t* pr, uint8_t* sr, uint8_t* pc, uint8_t* sc,
                            hipStream_t st) {
+  constexpr int NT = kRowColThreads, STR = kRowColStrips;
   int64_t ncolg;
-  const dim3 grid = rc_grid(M, K, ncolg), block(kRcThreads);
+  const dim3 grid = rc_grid<NT, STR>(M, K, ncolg), block(NT);
   if (!fos)
-    hipLaunchKernelGGL((k_rowcol<InT, false, false>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
+    hipLaunchKernelGGL((k_rowcol<InT, false, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
   else if (mse)
-    hipLaunchKernelGGL((k_rowcol<InT, true, true>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
+    hipLaunchKernelGGL((k_rowcol<InT, true, true, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
   else
-    hipLaunchKernelGGL((k_rowcol<InT, true, false>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
+    hipLaunchKernelGGL((k_rowcol<InT, true, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
   return (int)hipGetLastError();
 }
 
@@ -346,10 +350,11 @@ int launch_rowcol(const void* x, int in_bf16, int64_t M, int64_t K, const float*
 template <typename InT, bool MSE>
 static int launch_4over6_2d_t(const InT* x, const float* ga, float D, int64_t M, int64_t K,
                               uint8_t* pr, uint8_t* pc, uint8_t* ts, hipStream_t st) {
+  constexpr int NT = k46TileThreads, STR = k46TileStrips;
   int64_t ncolg;
-  const dim3 grid = rc_grid(M, K, ncolg), block(kRcThreads);
-  if (pc) hipLaunchKernelGGL((k_4over6_2d<InT, MSE, true>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg);
-  else hipLaunchKernelGGL((k_4over6_2d<InT, MSE, false>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg);
+  const dim3 grid = rc_grid<NT, STR>(M, K, ncolg), block(NT);
+  if (pc) hipLaunchKernelGGL((k_4over6_2d<InT, MSE, true, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg);
+  else hipLaunchKernelGGL((k_4over6_2d<InT, MSE, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg);
   return (int)hipGetLastError();
 }
 

@@ -16,13 +16,13 @@
 //    map-to-4 is kept iff its tile error is strictly lower.
 //
 // Mapping (both): a workgroup of NT lanes covers NT columns and walks down
-// up to STR strips of 16 rows (256 x 8 for k_rowcol, 512 x 16 for
+// up to STR strips of 16 rows (256 x 16 for k_rowcol, 512 x 16 for
 // k_4over6_2d).  In a strip it holds NT / 16 tiles side by side, four per
 // wave; lane (t, r) = (tid / 16, tid % 16) reads row r of tile
 // t (16 consecutive elements, 128-bit loads) and the next strip's row is
 // loaded while the current one is encoded.  Columnwise blocks are formed in
-// LDS: k_rowcol stages the tile's values (lane (t, c) then reads column c of
-// tile t), k_4over6_2d stages its codes (the same codes, transposed).  The
+// LDS: k_rowcol stages the tile's raw input (lane (t, c) then reads column c
+// of tile t), k_4over6_2d stages its codes (the same codes, transposed).  The
 // columnwise codes and scales of each column are gathered in LDS across the
 // strips and written out once per workgroup as whole column segments.
 //
@@ -37,10 +37,18 @@
 namespace nvfp4 {
 
 // Workgroup shapes (lanes = columns covered, 16-row strips per workgroup).
-constexpr int kRowColThreads = 256, kRowColStrips = 8;
+constexpr int kRowColThreads = 256, kRowColStrips = 16;
 constexpr int k46TileThreads = 512, k46TileStrips = 16;
-constexpr int kXRow = 20;                     // floats per staged row (16 used; 80 B keeps 16 B alignment)
-constexpr int kXTile = 16 * kXRow + 16;       // floats per staged tile (+16 shifts tiles across banks)
+
+// XCD-aware work order.  The dispatcher hands workgroup i to XCD i % 8, and
+// each XCD has its own L2.  With a grid of xcd_grid(n) workgroups, XCD x
+// takes work items x * ceil(n / 8) + 0, 1, 2, ... in dispatch order, so
+// neighbouring items (which write the two halves of shared output lines)
+// run in one L2.  Indices >= n are padding: such a workgroup exits at once.
+static int64_t xcd_grid(int64_t n) { return 8 * ((n + 7) / 8); }
+NV_DEV int64_t xcd_work_index(int64_t n) {
+  return (int64_t)(blockIdx.x & 7u) * ((n + 7) / 8) + (int64_t)(blockIdx.x >> 3);
+}
 
 // Max over the 16 lanes of a DPP row (every lane of the row gets it).
 NV_DEV uint32_t row16_max(uint32_t v) {
@@ -122,6 +130,31 @@ struct Raw16 {
   NV_DEV void to_f32(float v[16]) const { load16(reinterpret_cast<const InT*>(w), v); }
 };
 
+// LDS staging of one 16x16 tile of raw input for the columnwise blocks:
+// 16 rows of 16 elements, row stride kRow bytes, tile stride kTile bytes.
+// bf16 rows are dense (32 B); fp32 rows are padded to 80 B.  The extra 32 or
+// 64 bytes per tile put the four tiles of a wave in different bank windows
+// when each lane reads down its column.
+template <typename InT>
+struct StageTile {
+  static constexpr int kRow = sizeof(InT) == 2 ? 32 : 80;
+  static constexpr int kTile = 16 * kRow + 16 * (int)sizeof(InT);
+  NV_DEV static void put_row(uint8_t* tile, int r, const Raw16<InT>& raw) {
+    uint4* d = reinterpret_cast<uint4*>(tile + r * kRow);
+#pragma unroll
+    for (int i = 0; i < Raw16<InT>::kWords; ++i) d[i] = raw.w[i];
+  }
+  NV_DEV static void get_col(const uint8_t* tile, int c, float v[16]) {
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      if constexpr (sizeof(InT) == 2)
+        v[rr] = bits2f((uint32_t)*reinterpret_cast<const uint16_t*>(tile + rr * kRow + 2 * c) << 16);
+      else
+        v[rr] = *reinterpret_cast<const float*>(tile + rr * kRow + 4 * c);
+    }
+  }
+};
+
 // Write the column buffers of a workgroup: column cc of the workgroup owns
 // nst * 8 contiguous code bytes of its packed_col row (and nst scale bytes of
 // its scales_col row); 16 lanes serve one column.
@@ -144,12 +177,15 @@ __global__ __launch_bounds__(NT) void k_rowcol(
     const InT* __restrict__ x, const float* __restrict__ global_amax, float D, int64_t M, int64_t K,
     uint8_t* __restrict__ packed_row, uint8_t* __restrict__ scales_row,
     uint8_t* __restrict__ packed_col, uint8_t* __restrict__ scales_col, int64_t ncolg) {
-  __shared__ __attribute__((aligned(16))) float xs[(NT / 16) * kXTile];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[(NT / 16) * StageTile<InT>::kTile];
   __shared__ uint2 colbuf[NT * (STR + 1)];
   __shared__ uint8_t csbuf[NT * (STR + 1)];
   __shared__ float rhoT[FOS ? 128 : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
-  const int64_t sg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - sg * ncolg;
+  const int64_t nwork = ncolg * ((M / 16 + STR - 1) / STR);
+  const int64_t w = xcd_work_index(nwork);
+  if (w >= nwork) return;  // grid padding (uniform over the workgroup)
+  const int64_t sg = w / ncolg, cg = w - sg * ncolg;
   const int64_t col0 = cg * NT + 16 * t;
   const bool active = col0 < K;  // uniform over the 16 lanes of a tile
   const int64_t nstrips = M / 16;
@@ -163,7 +199,7 @@ __global__ __launch_bounds__(NT) void k_rowcol(
     if (threadIdx.x < 127) rhoT[threadIdx.x] = encode_reciprocal(e4m3_decode(threadIdx.x), S_dec);
     __syncthreads();
   }
-  float* stage = xs + t * kXTile;
+  uint8_t* stage = xs + t * StageTile<InT>::kTile;
 
   Raw16<InT> nxt;
   if (active) nxt.load(x + (sg * STR * 16 + r) * K + col0);
@@ -179,16 +215,13 @@ __global__ __launch_bounds__(NT) void k_rowcol(
                               : block_standard(v, mul, S_dec, c);
       *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c[0], c[1]);
       scales_row[row * (K / 16) + col0 / 16] = (uint8_t)sc;
-      float4* s4 = reinterpret_cast<float4*>(stage + r * kXRow);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s4[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+      StageTile<InT>::put_row(stage, r, cur);
     }
     __syncthreads();
     if (active) {
       // lane (t, c = r) now owns column c of tile t: rows 0..15 in order
       float v[16];
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) v[rr] = stage[rr * kXRow + r];
+      StageTile<InT>::get_col(stage, r, v);
       uint32_t c[2];
       const uint32_t sc = FOS ? block_fos<MSE>(v, S_enc, S_dec, A, D, rhoT, c)
                               : block_standard(v, mul, S_dec, c);
@@ -209,7 +242,10 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
   __shared__ uint4 stage[(NT / 16) * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (banks)
   __shared__ uint2 colbuf[COL ? NT * (STR + 1) : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
-  const int64_t sg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - sg * ncolg;
+  const int64_t nwork = ncolg * ((M / 16 + STR - 1) / STR);
+  const int64_t w = xcd_work_index(nwork);
+  if (w >= nwork) return;  // grid padding (uniform over the workgroup)
+  const int64_t sg = w / ncolg, cg = w - sg * ncolg;
   const int64_t col0 = cg * NT + 16 * t;
   const bool active = col0 < K;
   const int64_t nstrips = M / 16;
@@ -315,7 +351,7 @@ template <int NT, int STR>
 static dim3 rc_grid(int64_t M, int64_t K, int64_t& ncolg) {
   ncolg = (K + NT - 1) / NT;
   const int64_t nsg = (M / 16 + STR - 1) / STR;
-  return dim3((unsigned)(ncolg * nsg));
+  return dim3((unsigned)xcd_grid(ncolg * nsg));
 }
 
 template <typename InT>

@@ -2,9 +2,10 @@
 quantization and for four-over-six on 16x16 tiles with rowwise and
 columnwise outputs, through the C ABI.
 
-Shapes span several workgroups along both axes (a workgroup covers 256
-columns and 128 rows), ragged column tails (K not a multiple of 256) and
-single-tile tensors."""
+Shapes span several workgroups along both axes (a row + column workgroup
+covers 256 columns and 256 rows, a 16x16 four-over-six workgroup 512 columns
+and 256 rows), ragged row and column tails, grids padded for the XCD work
+order, and single-tile tensors."""
 import numpy as np
 import pytest
 import torch
@@ -16,7 +17,7 @@ from tests.test_gpu_parity import _specials
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(16, 16), (64, 96), (304, 304), (128, 4112), (272, 1040), (48, 512)]
+SHAPES = [(16, 16), (64, 96), (304, 304), (128, 4112), (272, 1040), (48, 512), (528, 784)]
 
 
 @pytest.fixture(autouse=True)

@@ -76,6 +76,16 @@ NV_DEV float tree16_sum(float e) {
   return e;
 }
 
+// True on every lane of a 16-lane tile iff f holds on all 16 of them.
+NV_DEV bool all16(bool f) {
+  int v = f ? 1 : 0;
+  v &= __shfl_xor(v, 8, 64);
+  v &= __shfl_xor(v, 4, 64);
+  v &= __shfl_xor(v, 2, 64);
+  v &= __shfl_xor(v, 1, 64);
+  return v != 0;
+}
+
 NV_DEV uint32_t absmax_bits16(const float v[16]) {
   uint32_t ab = 0;
 #pragma unroll
@@ -301,6 +311,9 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
     }
     // the decision is uniform over the tile (every lane holds the same tree totals)
     int pick = certified_pick<MSE, 8>(tree16_sum(E6), tree16_sum(E4), s6 * S_dec, s4 * S_dec, a);
+    // an undecided tile whose rows all have identical dequant values under
+    // both candidates (same_dequant16) is an exact tie: map-to-6
+    if (pick == -1 && all16(active && same_dequant16(c6, c4, s6, s4))) pick = 0;
     if (pick < 0) {  // exact row errors, then the same tree
       if (active) {
         if (pick == -1) {

@@ -164,6 +164,28 @@ NV_DEV float exact_error16(const float xv[16], const uint32_t c[2], float s, flo
   return E;
 }
 
+// Exact tie without the exact sums.  When s4 = 1.5 s6 exactly and every
+// map-to-6 value is exactly 1.5 times the map-to-4 value of the same element
+// (zeros of either sign included), the products q s of the two candidates are
+// equal as real numbers, so every later rounding of ((q s) A) / D, every
+// error term and the element-order sums agree: E_4 = E_6, which keeps
+// map-to-6.  Most exact ties of weight-like tensors are of this kind.
+NV_DEV bool same_dequant16(const uint32_t c6[2], const uint32_t c4[2], float s6, float s4) {
+  if (s4 != 1.5f * s6) return false;
+  bool same = true;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    nv_f2 p6[4], p4[4];
+    p6[0] = hw_fp4_values<0>(c6[w]); p4[0] = hw_fp4_values<0>(c4[w]);
+    p6[1] = hw_fp4_values<1>(c6[w]); p4[1] = hw_fp4_values<1>(c4[w]);
+    p6[2] = hw_fp4_values<2>(c6[w]); p4[2] = hw_fp4_values<2>(c4[w]);
+    p6[3] = hw_fp4_values<3>(c6[w]); p4[3] = hw_fp4_values<3>(c4[w]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) same = same && p6[b].x == 1.5f * p4[b].x && p6[b].y == 1.5f * p4[b].y;
+  }
+  return same;
+}
+
 // 1: map-to-4 proven, 0: map-to-6 proven, -1: undecided inside the range
 // guards (use exact_error16), -2: outside them (use the software
 // candidate).  kLog2N = 4 for a 1x16 block, 8 for a 16x16 tile (E6a / E4a
@@ -250,9 +272,13 @@ NV_DEV uint32_t fos_block(const float xv[16], float a, float S_enc, float S_dec,
   fos_candidates<MSE>(xv, rho6, rho4, c6, c4, E6a, E4a);
   int pick = certified_pick<MSE, 4>(E6a, E4a, s6 * S_dec, s4 * S_dec, a);
   if (pick == -1) {
-    const float E6 = exact_error16<MSE>(xv, c6, s6, A, D);
-    const float E4 = exact_error16<MSE>(xv, c4, s4, A, D);
-    pick = E4 < E6 ? 1 : 0;
+    if (same_dequant16(c6, c4, s6, s4)) {
+      pick = 0;
+    } else {
+      const float E6 = exact_error16<MSE>(xv, c6, s6, A, D);
+      const float E4 = exact_error16<MSE>(xv, c4, s4, A, D);
+      pick = E4 < E6 ? 1 : 0;
+    }
   } else if (pick == -2) {
     const float E6 = candidate<MSE>(xv, s6, rho6, A, D, c6[0], c6[1]);
     const float E4 = candidate<MSE>(xv, s4, rho4, A, D, c4[0], c4[1]);

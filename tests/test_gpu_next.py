@@ -197,3 +197,53 @@ def test_four_over_six_ties(shape, err, bound):
         assert_bitwise(to_np(t), wt, f"2d tiles A={A}")
         assert_bitwise(to_np(r), wr, f"2d rows A={A}")
         assert_bitwise(to_np(c), wc, f"2d cols A={A}")
+
+
+def identical_dequant_input(seed, M, K, A=3.0, broken=0.0):
+    """Blocks whose map-to-6 and map-to-4 candidates dequantize every element
+    to the same value, so their error sums tie exactly (zero error for the
+    on-grid values, nonzero for the off-grid ones).  Every block holds +-A
+    (so a = A, sigma6 = 256 and sigma4 = 384 at bound 256), the rest of its
+    elements are A times one of {1, 0.52, 0.5, 0.27, 0.25, 0.02, 0}: map-to-6
+    codes 6, 3, 3, 1.5, 1.5, 0, 0 and map-to-4 codes 4, 2, 2, 1, 1, 0, 0.  A
+    fraction `broken` of the 16x16 tiles get one element at 0.125 A (map-to-6
+    code 1 with error A / 24, map-to-4 code 0.5 with none), which breaks the
+    identity and makes map-to-4 win that block and tile."""
+    rng = np.random.default_rng(seed)
+    lv = np.array([1, 0.52, 0.5, 0.27, 0.25, 0.02, 0], np.float32)
+    x = rng.choice(lv, (M, K)) * rng.choice(np.array([-1, 1], np.float32), (M, K))
+    x[:, ::16] = rng.choice(np.array([-1, 1], np.float32), (M, K // 16))
+    t = x.reshape(M // 16, 16, K // 16, 16)
+    hit = rng.random((M // 16, K // 16)) < broken
+    t[:, 5, :, 7][hit] = np.float32(0.125)
+    import workloads
+    return workloads.bf16_bits((x * np.float32(A)).astype(np.float32))
+
+
+@pytest.mark.parametrize("err", ["mae", "mse"])
+@pytest.mark.parametrize("broken", [0.0, 0.3])
+@pytest.mark.parametrize("A0", [3.0, 0.0137, 1000.0])
+def test_four_over_six_identical_dequant_ties(err, broken, A0):
+    M, K = 96, 1040
+    x = identical_dequant_input(7 + int(broken * 10), M, K, A=A0, broken=broken)
+    xd = to_dev(x)
+    A = oracle.amax(x)
+    k6 = oracle.e4m3_encode(np.float32(256.0))
+    wp, ws = oracle.quantize_4over6(x, A, err_mode=err, bound=256.0)
+    # the tie rule keeps map-to-6 wherever the identity holds
+    assert (ws == k6).mean() > (0.99 if broken == 0.0 else 0.5)
+    assert (ws != k6).any() == (broken > 0)
+    p, s, _ = nv.quantize_4over6(xd, _ga(A), err_mode=err, e4m3_scale_bound=256, row_scaled=False)
+    assert_bitwise(to_np(s), ws, "1x16 scales")
+    assert_bitwise(to_np(p), wp, "1x16 codes")
+    want = oracle.quantize_rowcol(x, A, four_over_six=True, err_mode=err, bound=256.0)
+    got = nv.quantize_rowcol(xd, _ga(A), four_over_six=True, err_mode=err, e4m3_scale_bound=256)
+    for g, w, what in zip(got, want, ("pr", "sr", "pc", "sc")):
+        assert_bitwise(to_np(g), w, f"rowcol {what}")
+    wr, wc, wt = oracle.quantize_4over6_2d(x, A, err_mode=err, bound=256.0)
+    assert (wt == k6).mean() > (0.99 if broken == 0.0 else 0.3)
+    assert (wt != k6).any() == (broken > 0)
+    r, c, t = nv.quantize_4over6_2d(xd, _ga(A), err_mode=err, e4m3_scale_bound=256)
+    assert_bitwise(to_np(t), wt, "2d tiles")
+    assert_bitwise(to_np(r), wr, "2d rows")
+    assert_bitwise(to_np(c), wc, "2d cols")

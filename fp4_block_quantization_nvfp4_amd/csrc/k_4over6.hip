@@ -11,12 +11,15 @@
 // candidate with the strictly lower sum is stored; ties and NaN keep
 // map-to-6.
 //
-// Mapping: one workgroup per row (grid-stride over rows), one lane per
-// 16-element block of the row.  The per-row global amax is either read or
-// reduced by the workgroup in the same kernel (a first sweep over the row,
-// then the encode sweep re-reads the row, which is still in L2).  The work
-// is HBM streaming plus per-element VALU arithmetic; no LDS beyond the
-// workgroup reduction and no MFMA.
+// Generic kernel (fp32 input, or rows longer than 16384): one workgroup per
+// row (grid-stride over rows), one lane per 16-element block of the row.  The
+// per-row global amax is either read or reduced by the workgroup in the same
+// kernel (a first sweep over the row, then the encode sweep re-reads the row,
+// which is still in L2).  Each block takes fos_block: hardware encode of both
+// candidates, the certified choice, exact sums for undecided blocks and the
+// software candidate outside the range guards; the encode reciprocals of all
+// scale codes are tabulated in LDS per row.  The work is HBM streaming plus
+// per-element VALU arithmetic; no MFMA.
 #include "nvfp4_device.hpp"
 #include "nvfp4_fos.hpp"
 #include "nvfp4_launch.hpp"
@@ -48,6 +51,7 @@ __global__ __launch_bounds__(k46MaxThreads) void k_4over6(const InT* __restrict_
                                                           uint8_t* __restrict__ scales) {
   // MODE 1: one amax for the tensor; 2: row amax given; 3: row amax computed here.
   __shared__ float lds[k46MaxThreads / 64];
+  __shared__ float rhoT[128];
   const int64_t nbk = K / 16;
   for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
     const InT* xr = x + m * K;
@@ -58,7 +62,6 @@ __global__ __launch_bounds__(k46MaxThreads) void k_4over6(const InT* __restrict_
       float a = 0.0f, xv[16];
       for (int64_t b = threadIdx.x; b < nbk; b += blockDim.x) a = fmaxf(a, block_absmax16(xr + b * 16, xv));
       a = wave_max46(a);
-      __syncthreads();
       if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = a;
       __syncthreads();
       A = 0.0f;
@@ -67,22 +70,18 @@ __global__ __launch_bounds__(k46MaxThreads) void k_4over6(const InT* __restrict_
     }
     float S_enc, S_dec;
     global_scales(A, D, S_enc, S_dec);
+    for (int k = threadIdx.x; k < 127; k += blockDim.x) rhoT[k] = encode_reciprocal(e4m3_decode(k), S_dec);
+    __syncthreads();
     for (int64_t b = threadIdx.x; b < nbk; b += blockDim.x) {
       float xv[16];
       const float a = block_absmax16(xr + b * 16, xv);
-      const float sig6r = (a / 6.0f) * S_enc;
-      const float sig4r = sig6r * 1.5f;
-      const uint32_t k6 = e4m3_encode(fminf(sig6r, kE4m3Max));
-      const uint32_t k4 = e4m3_encode(fminf(sig4r, kE4m3Max));
-      const float s6 = e4m3_decode(k6), s4 = e4m3_decode(k4);
-      uint32_t a0, a1, b0, b1;
-      const float E6 = candidate<MSE>(xv, s6, encode_reciprocal(s6, S_dec), A, D, a0, a1);
-      const float E4 = candidate<MSE>(xv, s4, encode_reciprocal(s4, S_dec), A, D, b0, b1);
-      const bool pick4 = E4 < E6;
+      uint32_t c[2];
+      const uint32_t sbyte = fos_block<MSE>(xv, a, S_enc, S_dec, A, D, rhoT, c);
       const int64_t blk = m * nbk + b;
-      reinterpret_cast<uint2*>(packed)[blk] = pick4 ? make_uint2(b0, b1) : make_uint2(a0, a1);
-      scales[blk] = (uint8_t)(pick4 ? k4 : k6);
+      reinterpret_cast<uint2*>(packed)[blk] = make_uint2(c[0], c[1]);
+      scales[blk] = (uint8_t)sbyte;
     }
+    __syncthreads();  // lds and rhoT are rewritten for the next row
   }
 }
 

@@ -72,11 +72,12 @@ __global__ __launch_bounds__(k46MaxThreads) void k_4over6(const InT* __restrict_
     global_scales(A, D, S_enc, S_dec);
     for (int k = threadIdx.x; k < 127; k += blockDim.x) rhoT[k] = encode_reciprocal(e4m3_decode(k), S_dec);
     __syncthreads();
+    const bool lean = fos_row_in_range(A, S_dec);
     for (int64_t b = threadIdx.x; b < nbk; b += blockDim.x) {
       float xv[16];
-      const float a = block_absmax16(xr + b * 16, xv);
+      load16(xr + b * 16, xv);
       uint32_t c[2];
-      const uint32_t sbyte = fos_block<MSE>(xv, a, S_enc, S_dec, A, D, rhoT, c);
+      const uint32_t sbyte = fos_block_f32<MSE, MODE != 3>(xv, lean, S_enc, S_dec, A, D, rhoT, c);
       const int64_t blk = m * nbk + b;
       reinterpret_cast<uint2*>(packed)[blk] = make_uint2(c[0], c[1]);
       scales[blk] = (uint8_t)sbyte;
@@ -189,13 +190,18 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
       raw[j][1] = make_uint4(0, 0, 0, 0);
     }
   }
-  // NaN-dropping block amaxes as bf16 bit patterns
+  // NaN-dropping block amaxes as bf16 bit patterns; bit j of nan_blocks marks
+  // a block that holds a NaN (it never takes the lean path: the hardware
+  // encoder gives a negative NaN the code 0xF)
   uint32_t ab[R];
-  uint32_t lane_max = 0;
+  uint32_t lane_max = 0, nan_blocks = 0;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     ab[j] = absmax_bits(raw[j][0], raw[j][1]);
-    if (ab[j] > 0x7F80u) ab[j] = absmax_bits_nan_drop(raw[j][0], raw[j][1]);
+    if (ab[j] > 0x7F80u) {
+      nan_blocks |= 1u << j;
+      ab[j] = absmax_bits_nan_drop(raw[j][0], raw[j][1]);
+    }
     lane_max = ab[j] > lane_max ? ab[j] : lane_max;
   }
 
@@ -217,9 +223,9 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
   if (tid < 127) rhoT[tid] = encode_reciprocal(hw_e4m3_value<0>((uint32_t)tid), S_dec);
   __syncthreads();
 
-  // with the row's own amax (computed here) and a row in range, blocks take
-  // the lean fos_block_row; otherwise the general fos_block
-  const bool lean = MODE == 3 && fos_row_in_range(A, S_dec);
+  // in a row (or tensor) in range, plain blocks skip the range guards; with
+  // the row's own amax (computed here) every finite block has a <= A
+  const bool lean = fos_row_in_range(A, S_dec);
   uint2* prow = reinterpret_cast<uint2*>(packed) + row * nbk;
   uint8_t* srow = scales + row * nbk;
 #pragma unroll
@@ -229,8 +235,14 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
     float xv[16];
     unpack16(raw[j][0], raw[j][1], xv);
     uint32_t c[2];
-    const uint32_t sbyte = lean ? fos_block_row<MSE>(xv, ab[j], S_enc, S_dec, A, D, rhoT, c)
-                                : fos_block<MSE>(xv, bits2f(ab[j] << 16), S_enc, S_dec, A, D, rhoT, c);
+    // plain: no NaN, finite amax of at least 2^-117 and (row amax given or
+    // per tensor) a <= A; with the row's own amax a <= A always holds
+    const float a = bits2f(ab[j] << 16);
+    const bool plain = lean && !((nan_blocks >> j) & 1u) && ab[j] < 0x7F80u && ab[j] >= 0x0500u &&
+                       (MODE == 3 || a <= A);
+    const uint32_t sbyte = MODE == 3
+        ? fos_block_plain<MSE, false>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c)
+        : fos_block_plain<MSE, true>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c);
     prow[b] = make_uint2(c[0], c[1]);
     srow[b] = (uint8_t)sbyte;
   }

@@ -117,16 +117,6 @@ NV_DEV uint32_t block_standard(const float v[16], float mul, float S_dec, uint32
   return sc;
 }
 
-// Four-over-six 1x16 block (certified choice, exact fallback); returns the
-// chosen scale byte, codes in c.
-template <bool MSE>
-NV_DEV uint32_t block_fos(const float v[16], float S_enc, float S_dec, float A, float D,
-                          const float* rhoT, uint32_t c[2]) {
-  const uint32_t ab = absmax_bits16(v);
-  const float a = ab < 0x7F800000u ? bits2f(ab) : absmax_nan_drop16(v);
-  return fos_block<MSE>(v, a, S_enc, S_dec, A, D, rhoT, c);
-}
-
 // Raw input of 16 elements (uint4 words) and its conversion to fp32.
 template <typename InT>
 struct Raw16 {
@@ -205,6 +195,7 @@ __global__ __launch_bounds__(NT) void k_rowcol(
   float S_enc, S_dec;
   global_scales(A, D, S_enc, S_dec);
   const float mul = S_enc * (1.0f / 6.0f);
+  const bool lean = FOS && fos_row_in_range(A, S_dec);
   if (FOS) {
     if (threadIdx.x < 127) rhoT[threadIdx.x] = encode_reciprocal(e4m3_decode(threadIdx.x), S_dec);
     __syncthreads();
@@ -221,7 +212,7 @@ __global__ __launch_bounds__(NT) void k_rowcol(
       float v[16];
       cur.to_f32(v);
       uint32_t c[2];
-      const uint32_t sc = FOS ? block_fos<MSE>(v, S_enc, S_dec, A, D, rhoT, c)
+      const uint32_t sc = FOS ? fos_block_f32<MSE, true>(v, lean, S_enc, S_dec, A, D, rhoT, c)
                               : block_standard(v, mul, S_dec, c);
       *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c[0], c[1]);
       scales_row[row * (K / 16) + col0 / 16] = (uint8_t)sc;
@@ -233,7 +224,7 @@ __global__ __launch_bounds__(NT) void k_rowcol(
       float v[16];
       StageTile<InT>::get_col(stage, r, v);
       uint32_t c[2];
-      const uint32_t sc = FOS ? block_fos<MSE>(v, S_enc, S_dec, A, D, rhoT, c)
+      const uint32_t sc = FOS ? fos_block_f32<MSE, true>(v, lean, S_enc, S_dec, A, D, rhoT, c)
                               : block_standard(v, mul, S_dec, c);
       colbuf[(16 * t + r) * (STR + 1) + st] = make_uint2(c[0], c[1]);
       csbuf[(16 * t + r) * (STR + 1) + st] = (uint8_t)sc;

@@ -289,30 +289,28 @@ NV_DEV uint32_t fos_block(const float xv[16], float a, float S_enc, float S_dec,
   return pick ? k4 : k6;
 }
 
-// The same for a block of a row whose amax A is that row's own NaN-dropping
-// amax (so a <= A and sigma6 <= bound), in a row that passed
-// fos_row_in_range.  The range guards then reduce to a per-block flag: a
-// block is "plain" when its bf16 amax pattern ab16 is finite and at least
-// 2^-117 (a / 6 by the fast exact division) and its map-to-6 scale is not
-// zero; other blocks take the general fos_block.
+// The same without the range guards, for a "plain" block: it holds no NaN,
+// its amax a is finite with 2^-117 <= a <= A (a / 6 by the fast exact
+// division, and sigma6 <= bound), its map-to-6 scale is not zero, and its
+// tensor or row passed fos_row_in_range.  Then 2^-50 <= W6 <= W4 <= 2^50, a <= 2^50 and
+// every v_i <= 12, so every Z is finite and no guard of certified_pick is
+// needed.  Other blocks take the general fos_block.  With TIES, undecided
+// blocks first try same_dequant16.
 NV_DEV bool fos_row_in_range(float A, float S_dec) {
   return A <= 0x1p50f && S_dec >= 0x1p-41f && S_dec <= 0x1p41f;
 }
 
-template <bool MSE>
-NV_DEV uint32_t fos_block_row(const float xv[16], uint32_t ab16, float S_enc, float S_dec, float A,
-                              float D, const float* rhoT, uint32_t c[2]) {
-  const float a = bits2f(ab16 << 16);
+template <bool MSE, bool TIES>
+NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S_enc, float S_dec,
+                                float A, float D, const float* rhoT, uint32_t c[2]) {
   const uint32_t kk = fos_scale_codes(div_fast(a, 6.0f, 1.0f / 6.0f) * S_enc);
   const uint32_t k6 = kk & 0xFFu, k4 = kk >> 8;
-  if (ab16 >= 0x7F80u || ab16 < 0x0500u || k6 == 0u) return fos_block<MSE>(xv, a, S_enc, S_dec, A, D, rhoT, c);
+  if (!plain || k6 == 0u) return fos_block<MSE>(xv, a, S_enc, S_dec, A, D, rhoT, c);
   const float rho6 = rhoT[k6], rho4 = rhoT[k4];
   const float s6 = hw_e4m3_value<0>(kk), s4 = hw_e4m3_value<1>(kk);
   uint32_t c6[2], c4[2];
   float E6a, E4a;
   fos_candidates<MSE>(xv, rho6, rho4, c6, c4, E6a, E4a);
-  // In range: 2^-50 <= W6 <= W4 <= 2^50, a <= 2^50, every v_i <= 12, so Z is
-  // finite and no guard is needed (see certified_pick).
   const float W6 = s6 * S_dec, W4 = s4 * S_dec;
   const float Z6 = (MSE ? W6 * W6 : W6) * E6a;
   const float Z4 = (MSE ? W4 * W4 : W4) * E4a;
@@ -322,6 +320,8 @@ NV_DEV uint32_t fos_block_row(const float xv[16], uint32_t ab16, float S_enc, fl
     pick = 1;
   } else if (Z4 - B >= Z6) {
     pick = 0;
+  } else if (TIES && same_dequant16(c6, c4, s6, s4)) {
+    pick = 0;
   } else {
     const float E6 = exact_error16<MSE>(xv, c6, s6, A, D);
     const float E4 = exact_error16<MSE>(xv, c4, s4, A, D);
@@ -330,6 +330,30 @@ NV_DEV uint32_t fos_block_row(const float xv[16], uint32_t ab16, float S_enc, fl
   c[0] = pick ? c4[0] : c6[0];
   c[1] = pick ? c4[1] : c6[1];
   return pick ? k4 : k6;
+}
+
+// A block of 16 fp32 values with the tensor's (or row's) amax A and `lean` =
+// fos_row_in_range(A, S_dec): the largest magnitude bit pattern tells finite
+// blocks from blocks with a NaN or an infinity (those take fos_block with the
+// NaN-dropping amax); a finite block is plain when 2^-117 <= a <= A.
+template <bool MSE, bool TIES>
+NV_DEV uint32_t fos_block_f32(const float xv[16], bool lean, float S_enc, float S_dec, float A,
+                              float D, const float* rhoT, uint32_t c[2]) {
+  uint32_t ab = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t m = f2bits(xv[i]) & 0x7FFFFFFFu;
+    ab = m > ab ? m : ab;
+  }
+  if (ab < 0x7F800000u) {
+    const float a = bits2f(ab);
+    return fos_block_plain<MSE, TIES>(xv, a, lean && a >= 0x1p-117f && a <= A, S_enc, S_dec, A, D,
+                                      rhoT, c);
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xv[i]));
+  return fos_block<MSE>(xv, a, S_enc, S_dec, A, D, rhoT, c);
 }
 
 }  // namespace nvfp4

@@ -252,3 +252,82 @@ def test_empty_tensors():
     x2 = torch.empty((0, 32), dtype=torch.bfloat16, device="cuda")
     r, c, t = nv.quantize_2d(x2)
     assert r.shape == (0, 16)
+
+
+def _negative_nans(bf16):
+    """Finite blocks with NaNs of either sign in them (bf16 0xFFC0 / fp32
+    0xFFC00000 is a NaN with the sign bit set), an all-negative-NaN block and
+    a NaN next to an infinity.  Every NaN encodes as code 0x7 whatever its
+    sign, and the blocks' scales come from their NaN-dropping amaxes."""
+    M, K = 32, 128
+    x = wide_input(29, M, K, False, lo=-3, hi=3)
+    u = x.view(np.uint32)
+    neg, pos = np.uint32(0xFFC00000), np.uint32(0x7FC00000)
+    u[0, 5] = neg
+    u[1, 3] = neg
+    u[1, 9] = pos
+    u[2, 16:32] = neg
+    u[3, 40] = neg
+    x[3, 41] = np.inf
+    u[5::3, 7::11] = neg
+    u[17, 64:80] = neg
+    if bf16:
+        import workloads
+        b = workloads.bf16_bits(x)
+        b[np.isnan(x)] = np.where(np.signbit(x[np.isnan(x)]), 0xFFC0, 0x7FC0).astype(np.uint16)
+        return b
+    return x
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_negative_nan_blocks(bf16):
+    x = _negative_nans(bf16)
+    xf = oracle.bf16_bits_to_f32(x) if bf16 else x
+    assert np.signbit(xf[np.isnan(xf)]).sum() > 10
+    M, K = x.shape
+    xd = to_dev(x)
+    # the tensor holds an infinity: per-tensor paths also run with the largest
+    # finite magnitude as amax, so that NaN blocks sit among in-range blocks
+    A = np.float32(np.abs(xf[np.isfinite(xf)]).max())
+    assert oracle.amax(x) == np.inf
+    for st in (False, True):
+        wp, ws = oracle.quantize(x, stochastic=st, seed=3)
+        p, s = nv.quantize(xd, stochastic=st, seed=3)
+        assert_bitwise(to_np(s), ws, f"quantize scales sr={st}")
+        assert_bitwise(to_np(p), wp, f"quantize codes sr={st}")
+    for err in ("mae", "mse"):
+        Ar = oracle.amax(x, mode="row")
+        wp, ws = oracle.quantize_4over6(x, Ar, err_mode=err)
+        p, s, ga = nv.quantize_4over6(xd, None, err_mode=err, row_scaled=True)
+        assert_bitwise(to_np(ga), Ar, f"row amax {err}")
+        assert_bitwise(to_np(s), ws, f"4over6 row-computed scales {err}")
+        assert_bitwise(to_np(p), wp, f"4over6 row-computed codes {err}")
+        p, s, _ = nv.quantize_4over6(xd, torch.from_numpy(Ar).cuda(), err_mode=err)
+        assert_bitwise(to_np(s), ws, f"4over6 row-given scales {err}")
+        assert_bitwise(to_np(p), wp, f"4over6 row-given codes {err}")
+        for At in (A, oracle.amax(x)):
+            wp, ws = oracle.quantize_4over6(x, At, err_mode=err)
+            p, s, _ = nv.quantize_4over6(xd, torch.tensor([At], device="cuda"), err_mode=err,
+                                         row_scaled=False)
+            assert_bitwise(to_np(s), ws, f"4over6 tensor scales {err} A={At}")
+            assert_bitwise(to_np(p), wp, f"4over6 tensor codes {err} A={At}")
+        want = oracle.quantize_rowcol(x, A, four_over_six=True, err_mode=err, bound=256.0)
+        got = nv.quantize_rowcol(xd, torch.tensor([A], device="cuda"), four_over_six=True, err_mode=err,
+                                 e4m3_scale_bound=256)
+        for g, w, what in zip(got, want, ("pr", "sr", "pc", "sc")):
+            assert_bitwise(to_np(g), w, f"rowcol fos {what} {err}")
+        wr, wc, wt = oracle.quantize_4over6_2d(x, A, err_mode=err)
+        r, c, t = nv.quantize_4over6_2d(xd, torch.tensor([A], device="cuda"), err_mode=err)
+        assert_bitwise(to_np(t), wt, f"4over6 2d tiles {err}")
+        assert_bitwise(to_np(r), wr, f"4over6 2d rows {err}")
+        assert_bitwise(to_np(c), wc, f"4over6 2d cols {err}")
+    want = oracle.quantize_rowcol(x, A)
+    got = nv.quantize_rowcol(xd, torch.tensor([A], device="cuda"))
+    for g, w, what in zip(got, want, ("pr", "sr", "pc", "sc")):
+        assert_bitwise(to_np(g), w, f"rowcol std {what}")
+    for st in (False, True):
+        wr, wc, wt = oracle.quantize_2d(x, stochastic=st, seed=1, global_amax=A)
+        r, c, t = nv.quantize_2d(xd, torch.tensor([A], device="cuda"), stochastic=st, seed=1)
+        assert_bitwise(to_np(t), wt, f"2d tiles sr={st}")
+        assert_bitwise(to_np(r), wr, f"2d rows sr={st}")
+        assert_bitwise(to_np(c), wc, f"2d cols sr={st}")

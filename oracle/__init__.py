@@ -8,7 +8,9 @@ product.  The two share no code: the only common module is the seeded input
 generator (`workloads`), which holds none of the method's arithmetic.
 
 Arithmetic is numpy float32: every `+ - * /` is one IEEE binary32 operation
-rounded to nearest-even and never fused; `np.fmax`/`np.fmin` drop NaN.  bf16
+rounded to nearest-even and never fused; `np.fmin` drops a (quiet) NaN, and
+the NaN-dropping amax maps every NaN of the input, signalling ones included,
+to 0 before its max.  bf16
 values are handled as uint16 bit patterns.  Computation is vectorised over
 independent blocks only; within a block every step is taken in the order the
 pages give it.

@@ -53,9 +53,10 @@ def _nan_drop_absmax(t, axis):
     """NaN-dropping max of |t| over `axis`; an all-NaN group gives 0
     (four-over-six pull request, CuTe DSL kernel Design: NaN-dropping block
     amaxes, all-NaN group -> amax 0)."""
-    with np.errstate(invalid="ignore"):
-        m = np.fmax.reduce(np.abs(t), axis=axis)
-    return np.where(np.isnan(m), F32(0.0), m).astype(np.float32)
+    # every NaN counts as 0 before the max: np.fmax does not drop a
+    # signalling NaN (the running max turns into a NaN there and restarts)
+    a = np.abs(t)
+    return np.max(np.where(np.isnan(a), F32(0.0), a), axis=axis, initial=F32(0.0)).astype(np.float32)
 
 
 def _ef_add(x32, residual):

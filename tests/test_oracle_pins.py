@@ -346,3 +346,24 @@ def test_empty_inputs():
     p, s = oracle.quantize(x)
     assert p.shape == (0, 16) and s.shape == (0, 2)
     assert oracle.amax(x) == 0
+
+
+@pytest.mark.parametrize("nan_bits", [0x7F800001, 0xFF812345, 0x7FC00000, 0xFFC00000, 0x7FBFFFFF])
+@pytest.mark.parametrize("pos", [0, 5, 15])
+def test_nan_dropping_amax_drops_every_nan(nan_bits, pos):
+    """Block, row and tensor amaxes drop NaNs, signalling ones included,
+    wherever they sit: the amax is the max magnitude of the other elements
+    (and 0 for an all-NaN group).  Brute force over the finite elements."""
+    rng = np.random.default_rng(nan_bits % 1000 + pos)
+    x = (rng.standard_normal((3, 32)) * 100).astype(F32)
+    x[:, 7] = F32(-812.5)                      # the largest magnitude sits before the NaN
+    x.view(np.uint32)[:, 16 + pos] = nan_bits
+    x.view(np.uint32)[1, 8 + pos // 2] = nan_bits
+    x.view(np.uint32)[2, :16] = nan_bits       # an all-NaN block
+    fin = np.where(np.isnan(x), F32(0), np.abs(x))
+    assert np.array_equal(oracle.amax(x, mode="row"), fin.max(axis=1))
+    assert oracle.amax(x) == fin.max()
+    _, s = oracle.quantize(x)
+    want = oracle.e4m3_encode(np.fmin(fin.reshape(3, 2, 16).max(axis=2) / F32(6), F32(448)))
+    assert np.array_equal(s, want)
+    assert s[2, 0] == 0

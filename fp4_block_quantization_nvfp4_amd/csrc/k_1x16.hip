@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void k_quant1x16(
   } else {
     a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a = fmaxf(a, fabsf(xv[i]));
+    for (int i = 0; i < 4; ++i) a = fmaxf(a, abs_nan0(xv[i]));
     a = quad_fmax(a);
   }
 

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
       float l = 0.0f;
       if (active) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) l = fmaxf(l, fabsf(xv[i]));
+        for (int i = 0; i < 16; ++i) l = fmaxf(l, abs_nan0(xv[i]));
       }
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) l = fmaxf(l, __shfl_xor(l, off, 64));

@@ -39,7 +39,7 @@ NV_DEV float block_absmax16(const InT* p, float xv[16]) {
   load16(p, xv);
   float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xv[i]));
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, abs_nan0(xv[i]));
   return a;
 }
 

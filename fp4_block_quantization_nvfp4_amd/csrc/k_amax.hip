@@ -46,9 +46,18 @@ NV_DEV float group_absmax(const InT* x, const float* res, int64_t g) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) xv[i] = xv[i] + r[i];
   }
+  // magnitudes compare as integers; a NaN (above 0x7F800000) sends the
+  // group to the NaN-dropping form
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t b = f2bits(xv[i]) & 0x7FFFFFFFu;
+    m = b > m ? b : m;
+  }
+  if (m <= 0x7F800000u) return bits2f(m);
   float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xv[i]));
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, abs_nan0(xv[i]));
   return a;
 }
 

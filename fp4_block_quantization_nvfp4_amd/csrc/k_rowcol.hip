@@ -99,7 +99,7 @@ NV_DEV uint32_t absmax_bits16(const float v[16]) {
 NV_DEV float absmax_nan_drop16(const float v[16]) {
   float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(v[i]));
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, abs_nan0(v[i]));
   return a;
 }
 

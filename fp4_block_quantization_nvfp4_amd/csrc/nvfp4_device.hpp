@@ -20,6 +20,15 @@ constexpr float kE4m3Max = 448.0f;
 NV_DEV float bits2f(uint32_t u) { return __uint_as_float(u); }
 NV_DEV uint32_t f2bits(float f) { return __float_as_uint(f); }
 
+// |v| with every NaN (quiet or signalling, either sign) mapped to 0.  A
+// NaN-dropping maximum must not pass raw inputs to fmaxf: the hardware max
+// returns a quiet NaN when an operand is a signalling NaN.  After this map
+// every operand is a non-negative non-NaN float, for which fmaxf is exact.
+NV_DEV float abs_nan0(float v) {
+  const uint32_t m = f2bits(v) & 0x7FFFFFFFu;
+  return bits2f(m > 0x7F800000u ? 0u : m);
+}
+
 // ---------------------------------------------------------------- formats
 
 // e4m3 (OCP E4M3FN) byte of a scale sigma in [0, inf) (not NaN): round to

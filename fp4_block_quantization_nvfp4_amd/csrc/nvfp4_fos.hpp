@@ -352,7 +352,7 @@ NV_DEV uint32_t fos_block_f32(const float xv[16], bool lean, float S_enc, float 
   }
   float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(xv[i]));
+  for (int i = 0; i < 16; ++i) a = fmaxf(a, abs_nan0(xv[i]));
   return fos_block<MSE>(xv, a, S_enc, S_dec, A, D, rhoT, c);
 }
 

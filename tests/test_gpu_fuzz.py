@@ -109,7 +109,8 @@ def _ga(A):
     return torch.tensor([A], dtype=torch.float32, device="cuda")
 
 
-CASES = [(s, M, K, bf16, wide) for s, (M, K) in enumerate([(16, 64), (32, 272), (48, 1040), (64, 512), (96, 2064)])
+CASES = [(s, M, K, bf16, wide)
+         for s, (M, K) in enumerate([(16, 64), (32, 272), (48, 1040), (64, 512), (96, 2064), (16, 16400)])
          for bf16 in (False, True) for wide in (False, True)]
 
 
@@ -145,6 +146,19 @@ def test_fuzz_1x16_standard(seed, M, K, bf16, wide):
             want = oracle.dequantize(wp, ws, M, K, global_amax=A, scale_mode="tensor", out="f32")
             got = nv.dequantize(p, s, M, K, global_amax=_ga(A), out_dtype=torch.float32)
             assert_bitwise(to_np(got), want, f"dequantize A={A}")
+
+
+@pytest.mark.parametrize("seed,M,K,bf16,wide", CASES)
+def test_fuzz_amax(seed, M, K, bf16, wide):
+    x = fuzz_input(500 + seed, M, K, bf16, wide)
+    xd = to_dev(x)
+    r0 = fuzz_input(600 + seed, M, K, False, wide)
+    for r in (None, r0):
+        rd = None if r is None else to_dev(r)
+        assert_bitwise(to_np(nv.amax(xd, rd, "tensor")), np.array([oracle.amax(x, r)], np.float32),
+                       f"tensor amax res={r is not None}")
+        assert_bitwise(to_np(nv.amax(xd, rd, "row")), oracle.amax(x, r, mode="row"),
+                       f"row amax res={r is not None}")
 
 
 @pytest.mark.parametrize("seed,M,K,bf16,wide", CASES)

@@ -331,3 +331,55 @@ def test_negative_nan_blocks(bf16):
         assert_bitwise(to_np(t), wt, f"2d tiles sr={st}")
         assert_bitwise(to_np(r), wr, f"2d rows sr={st}")
         assert_bitwise(to_np(c), wc, f"2d cols sr={st}")
+
+
+@pytest.mark.parametrize("seed,step", [(0xFFFFFFFF, 0xFFFFFFFF), (0x80000000, 0), (0, 0x80000001),
+                                       (123456789, 987654321)])
+def test_stochastic_rounding_extreme_seeds(seed, step):
+    """Seeds and steps at the ends of their 32-bit range key the same draws
+    on both sides (1x16 quantize and qdq with error feedback, 2D)."""
+    M, K = 48, 272
+    for bf16 in (False, True):
+        x = wide_input(seed % 1000 + step % 1000, M, K, bf16, lo=-4, hi=4)
+        xd = to_dev(x)
+        wp, ws = oracle.quantize(x, stochastic=True, seed=seed, step=step)
+        p, s = nv.quantize(xd, stochastic=True, seed=seed, step=step)
+        assert_bitwise(to_np(s), ws, "scales")
+        assert_bitwise(to_np(p), wp, "codes")
+        r0 = (np.random.default_rng(3).standard_normal((M, K)) * 1e-3).astype(np.float32)
+        r_or = r0.copy()
+        wo = oracle.qdq(x, stochastic=True, residual=r_or, seed=seed, step=step)[0]
+        r = to_dev(r0)
+        o = nv.qdq(xd, stochastic=True, residual=r, seed=seed, step=step)
+        assert_bitwise(to_np(o), wo, "qdq out")
+        assert_bitwise(to_np(r), r_or, "qdq residual")
+        A = oracle.amax(x)
+        wr, wc, wt = oracle.quantize_2d(x, stochastic=True, seed=seed, step=step, global_amax=A)
+        rr, cc, tt = nv.quantize_2d(xd, torch.tensor([A], device="cuda"), stochastic=True, seed=seed, step=step)
+        assert_bitwise(to_np(tt), wt, "2d tiles")
+        assert_bitwise(to_np(rr), wr, "2d rows")
+        assert_bitwise(to_np(cc), wc, "2d cols")
+
+
+@pytest.mark.parametrize("K", [2048, 2064, 4096, 6144, 8192, 14336, 16368, 16384])
+def test_four_over_six_row_kernel_block_counts(K):
+    """The bf16 row kernel holds ceil(K / 2048) blocks per lane: row lengths
+    at and just past each multiple of 2048 columns, for every amax mode."""
+    M = 5
+    x = wide_input(K, M, K, True, lo=-6, hi=6)
+    xd = to_dev(x)
+    Ar = oracle.amax(x, mode="row")
+    for err in ("mae", "mse"):
+        wp, ws = oracle.quantize_4over6(x, Ar, err_mode=err)
+        p, s, ga = nv.quantize_4over6(xd, None, err_mode=err, row_scaled=True)
+        assert_bitwise(to_np(ga), Ar, "row amax")
+        assert_bitwise(to_np(s), ws, "row-computed scales")
+        assert_bitwise(to_np(p), wp, "row-computed codes")
+        p, s, _ = nv.quantize_4over6(xd, torch.from_numpy(Ar).cuda(), err_mode=err)
+        assert_bitwise(to_np(s), ws, "row-given scales")
+        assert_bitwise(to_np(p), wp, "row-given codes")
+        A = oracle.amax(x)
+        wp, ws = oracle.quantize_4over6(x, A, err_mode=err)
+        p, s, _ = nv.quantize_4over6(xd, torch.tensor([A], device="cuda"), err_mode=err, row_scaled=False)
+        assert_bitwise(to_np(s), ws, "tensor scales")
+        assert_bitwise(to_np(p), wp, "tensor codes")

@@ -16,8 +16,8 @@
 //    map-to-4 is kept iff its tile error is strictly lower.
 //
 // Mapping (both): a workgroup of NT lanes covers NT columns and walks down
-// up to STR strips of 16 rows (256 x 16 for k_rowcol, 512 x 16 for
-// k_4over6_2d).  In a strip it holds NT / 16 tiles side by side, four per
+// up to STR strips of 16 rows (256 x 16 for the standard k_rowcol, 128 x 16
+// for its four-over-six form, 512 x 16 for k_4over6_2d).  In a strip it holds NT / 16 tiles side by side, four per
 // wave; lane (t, r) = (tid / 16, tid % 16) reads row r of tile
 // t (16 consecutive elements, 128-bit loads) and the next strip's row is
 // loaded while the current one is encoded.  Columnwise blocks are formed in
@@ -37,7 +37,10 @@
 namespace nvfp4 {
 
 // Workgroup shapes (lanes = columns covered, 16-row strips per workgroup).
-constexpr int kRowColThreads = 256, kRowColStrips = 16;
+// The four-over-six row + column pass is VALU-heavy and gains from more
+// resident workgroups (128 columns: half the LDS); the standard pass is
+// bound by its memory pattern and prefers 256-byte row segments.
+constexpr int kRowColThreads = 256, kRowColFosThreads = 128, kRowColStrips = 16;
 constexpr int k46TileThreads = 512, k46TileStrips = 16;
 
 // XCD-aware work order.  The dispatcher hands workgroup i to XCD i % 8, and
@@ -362,15 +365,20 @@ template <typename InT>
 static int launch_rowcol_t(const InT* x, const float* ga, int fos, int mse, float D, int64_t M,
                            int64_t K, uint8_t* pr, uint8_t* sr, uint8_t* pc, uint8_t* sc,
                            hipStream_t st) {
-  constexpr int NT = kRowColThreads, STR = kRowColStrips;
+  constexpr int STR = kRowColStrips;
   int64_t ncolg;
-  const dim3 grid = rc_grid<NT, STR>(M, K, ncolg), block(NT);
-  if (!fos)
+  if (!fos) {
+    constexpr int NT = kRowColThreads;
+    const dim3 grid = rc_grid<NT, STR>(M, K, ncolg), block(NT);
     hipLaunchKernelGGL((k_rowcol<InT, false, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
-  else if (mse)
-    hipLaunchKernelGGL((k_rowcol<InT, true, true, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
-  else
-    hipLaunchKernelGGL((k_rowcol<InT, true, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
+  } else {
+    constexpr int NT = kRowColFosThreads;
+    const dim3 grid = rc_grid<NT, STR>(M, K, ncolg), block(NT);
+    if (mse)
+      hipLaunchKernelGGL((k_rowcol<InT, true, true, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
+    else
+      hipLaunchKernelGGL((k_rowcol<InT, true, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
+  }
   return (int)hipGetLastError();
 }
 

@@ -157,18 +157,30 @@ __global__ __launch_bounds__(kThreads) void k_quant1x16(
     }
   }
 
+  // bf16 input: streaming (nontemporal) stores measure faster; with fp32
+  // input (4096x4096 error-feedback steps) plain stores do
+  constexpr bool NT = sizeof(InT) == 2;
   if (CODES) {
-    reinterpret_cast<uint16_t*>(packed)[g] = (uint16_t)codes;
-    if ((threadIdx.x & 3) == 0) scales[g >> 2] = (uint8_t)sc;
+    if (NT) {
+      st_nt_u16(reinterpret_cast<uint16_t*>(packed) + g, codes);
+      if ((threadIdx.x & 3) == 0) st_nt_u8(scales + (g >> 2), sc);
+    } else {
+      reinterpret_cast<uint16_t*>(packed)[g] = (uint16_t)codes;
+      if ((threadIdx.x & 3) == 0) scales[g >> 2] = (uint8_t)sc;
+    }
   }
   if (HAS_RES) {
-    *reinterpret_cast<float4*>(residual + g * 4) =
-        make_float4(xv[0] - xh[0], xv[1] - xh[1], xv[2] - xh[2], xv[3] - xh[3]);
+    if (NT)
+      st_nt_f4(residual + g * 4, xv[0] - xh[0], xv[1] - xh[1], xv[2] - xh[2], xv[3] - xh[3]);
+    else
+      *reinterpret_cast<float4*>(residual + g * 4) =
+          make_float4(xv[0] - xh[0], xv[1] - xh[1], xv[2] - xh[2], xv[3] - xh[3]);
   }
   if (OUT == 1) {
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + g * 4) =
-        make_uint2(f32_to_bf16(xh[0]) | (f32_to_bf16(xh[1]) << 16),
-                   f32_to_bf16(xh[2]) | (f32_to_bf16(xh[3]) << 16));
+    const uint32_t lo = f32_to_bf16(xh[0]) | (f32_to_bf16(xh[1]) << 16);
+    const uint32_t hi = f32_to_bf16(xh[2]) | (f32_to_bf16(xh[3]) << 16);
+    if (NT) st_nt_u2(reinterpret_cast<uint16_t*>(out) + g * 4, lo, hi);
+    else *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + g * 4) = make_uint2(lo, hi);
   }
   if (OUT == 2) {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + g * 4) = make_float4(xh[0], xh[1], xh[2], xh[3]);

@@ -79,8 +79,8 @@ __global__ __launch_bounds__(k46MaxThreads) void k_4over6(const InT* __restrict_
       uint32_t c[2];
       const uint32_t sbyte = fos_block_f32<MSE, MODE != 3>(xv, lean, S_enc, S_dec, A, D, rhoT, c);
       const int64_t blk = m * nbk + b;
-      reinterpret_cast<uint2*>(packed)[blk] = make_uint2(c[0], c[1]);
-      scales[blk] = (uint8_t)sbyte;
+      st_nt_u2(reinterpret_cast<uint2*>(packed) + blk, c[0], c[1]);
+      st_nt_u8(scales + blk, sbyte);
     }
     __syncthreads();  // lds and rhoT are rewritten for the next row
   }
@@ -243,8 +243,8 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
     const uint32_t sbyte = MODE == 3
         ? fos_block_plain<MSE, false>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c)
         : fos_block_plain<MSE, true>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c);
-    prow[b] = make_uint2(c[0], c[1]);
-    srow[b] = (uint8_t)sbyte;
+    st_nt_u2(prow + b, c[0], c[1]);
+    st_nt_u8(srow + b, sbyte);
   }
 }
 

@@ -181,6 +181,28 @@ NV_DEV uint32_t hw_fp4_pair(uint32_t c, float a, float b) {
 }
 
 typedef float nv_f2 __attribute__((ext_vector_type(2)));
+typedef unsigned int nv_u32x2 __attribute__((ext_vector_type(2)));
+typedef float nv_f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (nontemporal) stores for outputs a kernel writes once and never
+// reads back: the lines are not retained in the caches, which speeds up the
+// write stream of these HBM-bound kernels.
+NV_DEV void st_nt_u8(uint8_t* p, uint32_t v) { __builtin_nontemporal_store((uint8_t)v, p); }
+NV_DEV void st_nt_u16(uint16_t* p, uint32_t v) { __builtin_nontemporal_store((uint16_t)v, p); }
+NV_DEV void st_nt_u2(void* p, uint32_t a, uint32_t b) {
+  nv_u32x2 v;
+  v.x = a;
+  v.y = b;
+  __builtin_nontemporal_store(v, reinterpret_cast<nv_u32x2*>(p));
+}
+NV_DEV void st_nt_f4(float* p, float a, float b, float c, float d) {
+  nv_f32x4 v;
+  v.x = a;
+  v.y = b;
+  v.z = c;
+  v.w = d;
+  __builtin_nontemporal_store(v, reinterpret_cast<nv_f32x4*>(p));
+}
 
 // e2m1 byte SEL of c -> the two exact values (low nibble first).
 template <int SEL>

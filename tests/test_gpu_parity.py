@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+import workloads
 import fp4_block_quantization_nvfp4_amd as nv
 from tests.gpu_util import assert_bitwise, need_gpu, to_dev, to_np, wide_input
 
@@ -78,6 +79,27 @@ def test_qdq_error_feedback(shape, bf16, stochastic, global_scale):
     want_f = oracle.qdq(x, stochastic=stochastic, residual=r0.copy(), seed=1, step=2,
                         global_amax=A, out="f32")[0]
     assert_bitwise(to_np(o3), want_f, "qdq f32 out")
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("where", ["first", "last", "middle", "second_unroll_slot", "tail"])
+def test_amax_tensor_positions(bf16, where):
+    """Per-tensor amax over 1024x1040 (about 0.5 M 16-byte chunks: every lane
+    takes several four-chunk steps and a remainder): the largest magnitude
+    planted at one position, NaNs of both signs and an infinity-free rest."""
+    M, K = 1024, 1040
+    rng = np.random.default_rng(11 if bf16 else 12)
+    x = (rng.standard_normal((M, K)) * 0.5).astype(np.float32)
+    flat = x.reshape(-1)
+    n = flat.size
+    pos = {"first": 0, "last": n - 1, "middle": n // 2 + 3, "second_unroll_slot": 524288 + 9,
+           "tail": n - 8 * 1000 - 5}[where]
+    flat[pos] = -37.75
+    for k in (1, 5000, n // 3, n - 2):
+        if k != pos:
+            flat[k] = np.float32(np.nan) if k % 2 else -np.float32(np.nan)
+    xi = workloads.bf16_bits(x) if bf16 else x
+    assert_bitwise(to_np(nv.amax(to_dev(xi), None, "tensor")), np.array([oracle.amax(xi)], np.float32))
 
 
 @pytest.mark.parametrize("shape", [(1, 16), (128, 320), (257, 4112), (2, 16384)])

@@ -228,6 +228,29 @@ def main():
     if not args.no_extra:
         line["extra"] = extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle,
                                         max(args.steps // 4, 10), max(args.warmup // 4, 3))
+        # the same workload with the other error measure (the configuration
+        # names both), parity-checked on the same sampled rows
+        other = "mse" if args.err == "mae" else "mae"
+        err_o = L.MSE if other == "mse" else L.MAE
+        args_o = [(a[:7] + (err_o,) + a[8:]) for a in call_args]
+
+        def step_o(i):
+            status = fn(*args_o[i % N_SETS])
+            if status:
+                L.check(status, "nvfp4_quantize_4over6")
+
+        step_o(0)
+        torch.cuda.synchronize()
+        wp, ws = oracle.quantize_4over6(x_bits[rows], A, err_mode=other, bound=bound)
+        check_rows(np, packed[0].cpu().numpy()[rows], wp, f"codes ({other})")
+        check_rows(np, scales[0].cpu().numpy()[rows], ws, f"scales ({other})")
+        ms_o = time_ms(torch, step_o, args.warmup, args.steps)
+        ms_ok = time_each_ms(torch, step_o, args.warmup, args.steps)
+        line["extra"][f"act_rows_8192x7168_4over6_{other}"] = {
+            "us": round(ms_o * 1e3, 3), "GB/s": round(algo / (ms_o * 1e-3) / 1e9, 2),
+            "frac_hbm": round(algo / (ms_o * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": algo,
+            "kernel_us": round(ms_ok * 1e3, 3),
+            "note": f"the metric workload with err_mode {other}; per-row amax computed in-pass"}
 
     if not args.no_cpu:
         # the oracle over whole rows of the same tensor, repeated until about

@@ -88,10 +88,11 @@ def time_ms(torch, fn, warmup, steps, host=None):
     return t0.elapsed_time(t1) / steps
 
 
-def time_each_ms(torch, fn, warmup, steps):
+def time_each_ms(torch, fn, warmup, steps, each=None):
     """Average ms of one call measured with a pair of events around each call
     on the launch stream (the kernel's own duration, without the gaps
-    between back-to-back launches)."""
+    between back-to-back launches).  If `each` is a list, it receives every
+    call's ms."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -101,7 +102,40 @@ def time_each_ms(torch, fn, warmup, steps):
         fn(i)
         ev[i][1].record()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / steps
+    d = [a.elapsed_time(b) for a, b in ev]
+    if each is not None:
+        each.extend(d)
+    return sum(d) / steps
+
+
+def percentile(v, q):
+    """q-th percentile (0..100) of a list, nearest rank."""
+    s = sorted(v)
+    return s[min(len(s) - 1, max(0, int(round(q / 100.0 * (len(s) - 1)))))]
+
+
+def copy_ceiling_gbs(torch, nbytes=1 << 30, reps=10):
+    """Plain device-to-device copy throughput (bytes read + written per
+    second) over two alternating pairs of buffers larger than the Infinity
+    Cache: the practical ceiling of a streaming kernel on this machine."""
+    n = nbytes // 4
+    bufs = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(4)]
+    for b in bufs:
+        b.fill_(1.0)
+    for i in range(3):
+        bufs[2 * (i % 2) + 1].copy_(bufs[2 * (i % 2)])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(reps):
+        bufs[2 * (i % 2) + 1].copy_(bufs[2 * (i % 2)])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del bufs
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def check_rows(np, got, want, what):
@@ -183,7 +217,8 @@ def main():
 
     host = {}
     ms = time_ms(torch, step, args.warmup, args.steps, host)
-    ms_kernel = time_each_ms(torch, step, args.warmup, args.steps)
+    each = []
+    ms_kernel = time_each_ms(torch, step, args.warmup, args.steps, each)
     algo = M * K * 2 + M * K // 2 + M * K // 16  # 150,470,656 B
     gbs = algo / (ms * 1e-3) / 1e9
     kgbs = algo / (ms_kernel * 1e-3) / 1e9
@@ -222,6 +257,8 @@ def main():
             "avg_launch_us": round(ms_kernel * 1e3, 3),
             "timing": "events around each launch on the launch stream; value uses the whole timed region",
             "host_submit_us_per_launch": round(host["us_per_call"], 3),
+            "launch_us_p10_median_p90": [round(percentile(each, q) * 1e3, 3) for q in (10, 50, 90)],
+            "copy_ceiling_GBs": round(copy_ceiling_gbs(torch), 1),
         },
     }
 

@@ -1,5 +1,5 @@
-"""Host-side logic of bench.py (no GPU): the one-GPU guard and the reader of
-the committed HBM-traffic counter summary."""
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the reader of
+the committed HBM-traffic counter summary and the percentile helper."""
 import os
 import subprocess
 import sys
@@ -37,3 +37,13 @@ def test_source_hash_covers_the_kernel_and_its_headers():
     h = bench.src_hash()
     assert len(h) == 16 and int(h, 16) >= 0
     assert h == bench.src_hash()
+
+
+def test_percentile_is_nearest_rank():
+    v = [7.0, 1.0, 3.0, 9.0, 5.0]
+    assert bench.percentile(v, 0) == 1.0
+    assert bench.percentile(v, 50) == 5.0
+    assert bench.percentile(v, 100) == 9.0
+    assert bench.percentile(list(range(101)), 10) == 10
+    assert bench.percentile(list(range(101)), 90) == 90
+    assert bench.percentile([4.0], 90) == 4.0

@@ -97,8 +97,9 @@ __global__ __launch_bounds__(k46MaxThreads) void k_4over6(const InT* __restrict_
 //  * The candidate choice is certified from error sums in the scaled
 //    domain (fos_block); only undecided blocks compute the per-element
 //    dequant values with true divisions.
-//  * The encode reciprocals of all 127 scale codes are tabulated in LDS once
-//    per row (one correctly rounded reciprocal per lane).
+//  * The encode reciprocals of all 127 scale codes, and the products
+//    W = s * S_dec of the error bound, are tabulated in LDS once per row
+//    (one correctly rounded reciprocal per lane).
 //  * a / 6 uses reciprocal-multiply plus one exact FMA remainder correction
 //    where that is proven correctly rounded, else the true division.
 // A two-wave workgroup owns one row: it loads the row (R blocks per lane)
@@ -171,6 +172,7 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
                                                              uint8_t* __restrict__ packed,
                                                              uint8_t* __restrict__ scales) {
   __shared__ float rhoT[128];
+  __shared__ float WT[128];
   __shared__ uint32_t red[kRowThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
@@ -220,7 +222,11 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
   }
   float S_enc, S_dec;
   global_scales(A, D, S_enc, S_dec);
-  if (tid < 127) rhoT[tid] = encode_reciprocal(hw_e4m3_value<0>((uint32_t)tid), S_dec);
+  if (tid < 127) {
+    const float s = hw_e4m3_value<0>((uint32_t)tid);
+    rhoT[tid] = encode_reciprocal(s, S_dec);
+    WT[tid] = s * S_dec;
+  }
   __syncthreads();
 
   // in a row (or tensor) in range, plain blocks skip the range guards; with
@@ -241,8 +247,8 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
     const bool plain = lean && !((nan_blocks >> j) & 1u) && ab[j] < 0x7F80u && ab[j] >= 0x0500u &&
                        (MODE == 3 || a <= A);
     const uint32_t sbyte = MODE == 3
-        ? fos_block_plain<MSE, false>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c)
-        : fos_block_plain<MSE, true>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c);
+        ? fos_block_plain<MSE, false>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c, WT)
+        : fos_block_plain<MSE, true>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c, WT);
     st_nt_u2(prow + b, c[0], c[1]);
     st_nt_u8(srow + b, sbyte);
   }

@@ -300,29 +300,36 @@ NV_DEV bool fos_row_in_range(float A, float S_dec) {
   return A <= 0x1p50f && S_dec >= 0x1p-41f && S_dec <= 0x1p41f;
 }
 
+// WT, when not null, holds W = s * S_dec for every scale code (the same
+// product the block would form), tabulated per row beside rhoT.  The margin
+// is formed as 2^-15 (a + (Z4 + Z6)) + 2^-90 (a^2 for MSE): the same bound
+// as in certified_pick with one rounding of the sum, far inside its 2.6x
+// safety factor.
 template <bool MSE, bool TIES>
 NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S_enc, float S_dec,
-                                float A, float D, const float* rhoT, uint32_t c[2]) {
+                                float A, float D, const float* rhoT, uint32_t c[2],
+                                const float* WT = nullptr) {
   const uint32_t kk = fos_scale_codes(div_fast(a, 6.0f, 1.0f / 6.0f) * S_enc);
   const uint32_t k6 = kk & 0xFFu, k4 = kk >> 8;
   if (!plain || k6 == 0u) return fos_block<MSE>(xv, a, S_enc, S_dec, A, D, rhoT, c);
   const float rho6 = rhoT[k6], rho4 = rhoT[k4];
-  const float s6 = hw_e4m3_value<0>(kk), s4 = hw_e4m3_value<1>(kk);
   uint32_t c6[2], c4[2];
   float E6a, E4a;
   fos_candidates<MSE>(xv, rho6, rho4, c6, c4, E6a, E4a);
-  const float W6 = s6 * S_dec, W4 = s4 * S_dec;
+  const float W6 = WT ? WT[k6] : hw_e4m3_value<0>(kk) * S_dec;
+  const float W4 = WT ? WT[k4] : hw_e4m3_value<1>(kk) * S_dec;
   const float Z6 = (MSE ? W6 * W6 : W6) * E6a;
   const float Z4 = (MSE ? W4 * W4 : W4) * E4a;
-  const float B = 0x1p-15f * (MSE ? a * a : a) + 0x1p-15f * (Z4 + Z6) + 0x1p-90f;
+  const float B = 0x1p-15f * ((MSE ? a * a : a) + (Z4 + Z6)) + 0x1p-90f;
   int pick;
   if (Z4 + B < Z6) {
     pick = 1;
   } else if (Z4 - B >= Z6) {
     pick = 0;
-  } else if (TIES && same_dequant16(c6, c4, s6, s4)) {
+  } else if (TIES && same_dequant16(c6, c4, hw_e4m3_value<0>(kk), hw_e4m3_value<1>(kk))) {
     pick = 0;
   } else {
+    const float s6 = hw_e4m3_value<0>(kk), s4 = hw_e4m3_value<1>(kk);
     const float E6 = exact_error16<MSE>(xv, c6, s6, A, D);
     const float E4 = exact_error16<MSE>(xv, c4, s4, A, D);
     pick = E4 < E6 ? 1 : 0;

@@ -247,8 +247,8 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
     const bool plain = lean && !((nan_blocks >> j) & 1u) && ab[j] < 0x7F80u && ab[j] >= 0x0500u &&
                        (MODE == 3 || a <= A);
     const uint32_t sbyte = MODE == 3
-        ? fos_block_plain<MSE, false>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c, WT)
-        : fos_block_plain<MSE, true>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c, WT);
+        ? fos_block_plain<MSE, false, true>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c, WT)
+        : fos_block_plain<MSE, true, true>(xv, a, plain, S_enc, S_dec, A, D, rhoT, c, WT);
     st_nt_u2(prow + b, c[0], c[1]);
     st_nt_u8(srow + b, sbyte);
   }

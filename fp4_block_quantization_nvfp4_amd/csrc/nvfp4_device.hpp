@@ -175,6 +175,16 @@ NV_DEV float div_guarded(float n, float D, float rD) {
 // +-6; scale operand 1.0 means no scaling) into byte SEL of c.  Equal to the
 // software encoder for every finite and infinite input; a negative NaN gives
 // 0xF instead of 0x7, so callers keep NaN inputs off this path.
+// A 32-bit register whose starting contents do not matter: the empty asm
+// statement emits no instruction and only marks the register as written.
+// Code words whose four bytes are all written by hw_fp4_pair<0..3> start
+// from it, so no register clear is issued per word.
+NV_DEV uint32_t any_u32() {
+  uint32_t v;
+  asm volatile("" : "=v"(v));
+  return v;
+}
+
 template <int SEL>
 NV_DEV uint32_t hw_fp4_pair(uint32_t c, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, a, b, 1.0f, SEL);

@@ -225,8 +225,9 @@ NV_DEV void fos_pair(float x0, float x1, float rho, uint32_t& c, float& E) {
 
 template <bool MSE>
 NV_DEV void fos_candidate(const float xv[16], float rho, uint32_t c[2], float& E) {
-  c[0] = 0u;
-  c[1] = 0u;
+  // the four conversions of each word write all four of its bytes
+  c[0] = any_u32();
+  c[1] = any_u32();
   E = 0.0f;
   fos_pair<MSE, 0>(xv[0], xv[1], rho, c[0], E);
   fos_pair<MSE, 1>(xv[2], xv[3], rho, c[0], E);
@@ -300,12 +301,12 @@ NV_DEV bool fos_row_in_range(float A, float S_dec) {
   return A <= 0x1p50f && S_dec >= 0x1p-41f && S_dec <= 0x1p41f;
 }
 
-// WT, when not null, holds W = s * S_dec for every scale code (the same
-// product the block would form), tabulated per row beside rhoT.  The margin
+// With WTAB, WT holds W = s * S_dec for every scale code (the same product
+// the block would form), tabulated per row beside rhoT.  The margin
 // is formed as 2^-15 (a + (Z4 + Z6)) + 2^-90 (a^2 for MSE): the same bound
 // as in certified_pick with one rounding of the sum, far inside its 2.6x
 // safety factor.
-template <bool MSE, bool TIES>
+template <bool MSE, bool TIES, bool WTAB = false>
 NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S_enc, float S_dec,
                                 float A, float D, const float* rhoT, uint32_t c[2],
                                 const float* WT = nullptr) {
@@ -316,8 +317,8 @@ NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S
   uint32_t c6[2], c4[2];
   float E6a, E4a;
   fos_candidates<MSE>(xv, rho6, rho4, c6, c4, E6a, E4a);
-  const float W6 = WT ? WT[k6] : hw_e4m3_value<0>(kk) * S_dec;
-  const float W4 = WT ? WT[k4] : hw_e4m3_value<1>(kk) * S_dec;
+  const float W6 = WTAB ? WT[k6] : hw_e4m3_value<0>(kk) * S_dec;
+  const float W4 = WTAB ? WT[k4] : hw_e4m3_value<1>(kk) * S_dec;
   const float Z6 = (MSE ? W6 * W6 : W6) * E6a;
   const float Z4 = (MSE ? W4 * W4 : W4) * E4a;
   const float B = 0x1p-15f * ((MSE ? a * a : a) + (Z4 + Z6)) + 0x1p-90f;

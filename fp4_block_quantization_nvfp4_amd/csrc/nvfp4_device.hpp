@@ -259,7 +259,7 @@ NV_DEV uint32_t hw_fp4_sr_word(const float* x, float rho, const uint32_t* nw) {
 // gfx950 fp32 -> e4m3 of two scales in [0, 448] (bytes 0 and 1): equal to
 // e4m3_encode on every float32 in that range (checked exhaustively).
 NV_DEV uint32_t hw_e4m3_pair(float a, float b) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)any_u32(), false) & 0xFFFFu;
 }
 
 // gfx950 e4m3 byte SEL of c -> fp32: equal to e4m3_decode on every code

@@ -302,10 +302,11 @@ NV_DEV bool fos_row_in_range(float A, float S_dec) {
 }
 
 // With WTAB, WT holds W = s * S_dec for every scale code (the same product
-// the block would form), tabulated per row beside rhoT.  The margin
-// is formed as 2^-15 (a + (Z4 + Z6)) + 2^-90 (a^2 for MSE): the same bound
-// as in certified_pick with one rounding of the sum, far inside its 2.6x
-// safety factor.
+// the block would form), tabulated per row beside rhoT.  The margin is
+// formed as fma(a + (Z4 + Z6), 2^-15, 2^-90) (a^2 for MSE), and the test
+// compares fl(Z6 - Z4) with +-B: the same bound as in certified_pick up to
+// a few roundings of relative size 2^-24, far inside its 2.6x safety factor
+// (fl(Z6 - Z4) > B implies Z6 - Z4 > B / (1 + 2^-24)).
 template <bool MSE, bool TIES, bool WTAB = false>
 NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S_enc, float S_dec,
                                 float A, float D, const float* rhoT, uint32_t c[2],
@@ -321,11 +322,12 @@ NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S
   const float W4 = WTAB ? WT[k4] : hw_e4m3_value<1>(kk) * S_dec;
   const float Z6 = (MSE ? W6 * W6 : W6) * E6a;
   const float Z4 = (MSE ? W4 * W4 : W4) * E4a;
-  const float B = 0x1p-15f * ((MSE ? a * a : a) + (Z4 + Z6)) + 0x1p-90f;
+  const float B = __builtin_fmaf((MSE ? a * a : a) + (Z4 + Z6), 0x1p-15f, 0x1p-90f);
+  const float dZ = Z6 - Z4;
   int pick;
-  if (Z4 + B < Z6) {
+  if (dZ > B) {
     pick = 1;
-  } else if (Z4 - B >= Z6) {
+  } else if (dZ <= -B) {
     pick = 0;
   } else if (TIES && same_dequant16(c6, c4, hw_e4m3_value<0>(kk), hw_e4m3_value<1>(kk))) {
     pick = 0;

@@ -311,8 +311,9 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
     if (pick < 0) {  // exact row errors, then the same tree
       if (active) {
         if (pick == -1) {
-          E6 = exact_error16<MSE>(v, c6, s6, A, D);
-          E4 = exact_error16<MSE>(v, c4, s4, A, D);
+          const float rD = recip_in_place(D);
+          E6 = exact_error16<MSE>(v, c6, s6, A, D, rD);
+          E4 = exact_error16<MSE>(v, c4, s4, A, D, rD);
         } else {
           E6 = candidate<MSE>(v, s6, rho6, A, D, c6[0], c6[1]);
           E4 = candidate<MSE>(v, s4, rho4, A, D, c4[0], c4[1]);

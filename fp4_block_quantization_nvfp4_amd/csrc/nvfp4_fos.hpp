@@ -127,6 +127,14 @@ NV_DEV float approx_error16(const float v[16], const uint32_t c[2]) {
   return E;
 }
 
+// 1 / D computed where it is written: the empty asm statement hides D's
+// value, so the division is not hoisted out of the rare exact path into the
+// prologue of every wave.
+NV_DEV float recip_in_place(float D) {
+  asm volatile("" : "+v"(D));
+  return 1.0f / D;
+}
+
 // Exact element-order error sum of one candidate with codes c (finite
 // inputs, scale s, inside the range guards).  A code value is q = mu 2^k
 // with mu in {1, 1.5}, so fl(q s A) = 2^k fl(mu s A) and
@@ -134,9 +142,10 @@ NV_DEV float approx_error16(const float v[16], const uint32_t c[2]) {
 // normal: two correctly rounded divisions per candidate instead of one per
 // element.  2^k is q's exponent field (0 for q = 0), mu is its top mantissa
 // bit.
+// rD = 1 / D (see recip_in_place).
 template <bool MSE>
-NV_DEV float exact_error16(const float xv[16], const uint32_t c[2], float s, float A, float D) {
-  const float rD = 1.0f / D;
+NV_DEV float exact_error16(const float xv[16], const uint32_t c[2], float s, float A, float D,
+                           float rD) {
   const float Q1 = div_guarded(s * A, D, rD);
   const float Q15 = div_guarded((1.5f * s) * A, D, rD);
   float E = 0.0f;
@@ -276,8 +285,9 @@ NV_DEV uint32_t fos_block(const float xv[16], float a, float S_enc, float S_dec,
     if (same_dequant16(c6, c4, s6, s4)) {
       pick = 0;
     } else {
-      const float E6 = exact_error16<MSE>(xv, c6, s6, A, D);
-      const float E4 = exact_error16<MSE>(xv, c4, s4, A, D);
+      const float rD = recip_in_place(D);
+      const float E6 = exact_error16<MSE>(xv, c6, s6, A, D, rD);
+      const float E4 = exact_error16<MSE>(xv, c4, s4, A, D, rD);
       pick = E4 < E6 ? 1 : 0;
     }
   } else if (pick == -2) {
@@ -333,8 +343,9 @@ NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S
     pick = 0;
   } else {
     const float s6 = hw_e4m3_value<0>(kk), s4 = hw_e4m3_value<1>(kk);
-    const float E6 = exact_error16<MSE>(xv, c6, s6, A, D);
-    const float E4 = exact_error16<MSE>(xv, c4, s4, A, D);
+    const float rD = recip_in_place(D);
+    const float E6 = exact_error16<MSE>(xv, c6, s6, A, D, rD);
+    const float E4 = exact_error16<MSE>(xv, c4, s4, A, D, rD);
     pick = E4 < E6 ? 1 : 0;
   }
   c[0] = pick ? c4[0] : c6[0];

@@ -184,6 +184,7 @@ __global__ __launch_bounds__(NT) void k_rowcol(
   __shared__ uint2 colbuf[NT * (STR + 1)];
   __shared__ uint8_t csbuf[NT * (STR + 1)];
   __shared__ float rhoT[FOS ? 128 : 1];
+  __shared__ float WT[FOS ? 128 : 1];  // W = s * S_dec per scale code
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
   const int64_t nwork = ncolg * ((M / 16 + STR - 1) / STR);
   const int64_t w = xcd_work_index(nwork);
@@ -200,7 +201,11 @@ __global__ __launch_bounds__(NT) void k_rowcol(
   const float mul = S_enc * (1.0f / 6.0f);
   const bool lean = FOS && fos_row_in_range(A, S_dec);
   if (FOS) {
-    if (threadIdx.x < 127) rhoT[threadIdx.x] = encode_reciprocal(e4m3_decode(threadIdx.x), S_dec);
+    if (threadIdx.x < 127) {
+      const float s = e4m3_decode(threadIdx.x);
+      rhoT[threadIdx.x] = encode_reciprocal(s, S_dec);
+      WT[threadIdx.x] = s * S_dec;
+    }
     __syncthreads();
   }
   uint8_t* stage = xs + t * StageTile<InT>::kTile;
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(NT) void k_rowcol(
       float v[16];
       cur.to_f32(v);
       uint32_t c[2];
-      const uint32_t sc = FOS ? fos_block_f32<MSE, true>(v, lean, S_enc, S_dec, A, D, rhoT, c)
+      const uint32_t sc = FOS ? fos_block_f32<MSE, true, true>(v, lean, S_enc, S_dec, A, D, rhoT, c, WT)
                               : block_standard(v, mul, S_dec, c);
       *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c[0], c[1]);
       scales_row[row * (K / 16) + col0 / 16] = (uint8_t)sc;
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(NT) void k_rowcol(
       float v[16];
       StageTile<InT>::get_col(stage, r, v);
       uint32_t c[2];
-      const uint32_t sc = FOS ? fos_block_f32<MSE, true>(v, lean, S_enc, S_dec, A, D, rhoT, c)
+      const uint32_t sc = FOS ? fos_block_f32<MSE, true, true>(v, lean, S_enc, S_dec, A, D, rhoT, c, WT)
                               : block_standard(v, mul, S_dec, c);
       colbuf[(16 * t + r) * (STR + 1) + st] = make_uint2(c[0], c[1]);
       csbuf[(16 * t + r) * (STR + 1) + st] = (uint8_t)sc;

@@ -357,9 +357,9 @@ NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S
 // fos_row_in_range(A, S_dec): the largest magnitude bit pattern tells finite
 // blocks from blocks with a NaN or an infinity (those take fos_block with the
 // NaN-dropping amax); a finite block is plain when 2^-117 <= a <= A.
-template <bool MSE, bool TIES>
+template <bool MSE, bool TIES, bool WTAB = false>
 NV_DEV uint32_t fos_block_f32(const float xv[16], bool lean, float S_enc, float S_dec, float A,
-                              float D, const float* rhoT, uint32_t c[2]) {
+                              float D, const float* rhoT, uint32_t c[2], const float* WT = nullptr) {
   uint32_t ab = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -368,8 +368,8 @@ NV_DEV uint32_t fos_block_f32(const float xv[16], bool lean, float S_enc, float 
   }
   if (ab < 0x7F800000u) {
     const float a = bits2f(ab);
-    return fos_block_plain<MSE, TIES>(xv, a, lean && a >= 0x1p-117f && a <= A, S_enc, S_dec, A, D,
-                                      rhoT, c);
+    return fos_block_plain<MSE, TIES, WTAB>(xv, a, lean && a >= 0x1p-117f && a <= A, S_enc, S_dec, A,
+                                            D, rhoT, c, WT);
   }
   float a = 0.0f;
 #pragma unroll

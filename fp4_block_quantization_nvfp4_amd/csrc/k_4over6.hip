@@ -179,18 +179,17 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
   const int nbk = (int)(K >> 4);
   const uint16_t* xr = x + row * K;
 
+  // A lane past the row's last block loads the last block again (no branch,
+  // no register clear): its amax cannot exceed the row's and it encodes
+  // nothing.
   uint4 raw[R][2];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const int b = tid + kRowThreads * j;
-    if (b < nbk) {
-      const uint4* p = reinterpret_cast<const uint4*>(xr + (int64_t)b * 16);
-      raw[j][0] = p[0];
-      raw[j][1] = p[1];
-    } else {
-      raw[j][0] = make_uint4(0, 0, 0, 0);
-      raw[j][1] = make_uint4(0, 0, 0, 0);
-    }
+    const uint32_t off = (uint32_t)(b < nbk ? b : nbk - 1) * 32u;  // bytes; nbk <= 1024 here
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(xr) + off);
+    raw[j][0] = p[0];
+    raw[j][1] = p[1];
   }
   // NaN-dropping block amaxes as bf16 bit patterns; bit j of nan_blocks marks
   // a block that holds a NaN (it never takes the lean path: the hardware

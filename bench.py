@@ -410,7 +410,16 @@ def extra_workloads(np, torch, nv, L, lib, stream, workloads, oracle, steps, war
         rec(f"weight_2d_7168x18432_rowcol_1x16_{'4over6_mae' if fos else 'standard'}", ms_rc,
             n2 * 2 + n2 + n2 // 8, "bf16 in, rowwise + columnwise codes and 1x16 scales")
     rec("weight_2d_7168x18432_amax", ms_amax, n2 * 2, "per-tensor amax, two passes")
-    rec("weight_2d_7168x18432_amax_plus_2d", ms_amax + ms_2d, n2 * 2 * 2 + n2 + n2 // 256, "end to end")
+    def amax_then_2d(i):
+        j = i % 2
+        lib.nvfp4_amax(wd[j].data_ptr(), L.BF16, Mt, Kt, None, L.SCALE_TENSOR, ga.data_ptr(), wsb.data_ptr(),
+                       wsz, stream)
+        lib.nvfp4_quantize_2d(wd[j].data_ptr(), L.BF16, Mt, Kt, ga.data_ptr(), 1, 0, 0, 0, pr[j].data_ptr(),
+                              pc[j].data_ptr(), ts[j].data_ptr(), stream)
+
+    ms_pair = time_ms(torch, amax_then_2d, warmup, steps)
+    rec("weight_2d_7168x18432_amax_plus_2d", ms_pair, n2 * 2 * 2 + n2 + n2 // 256,
+        "end to end: the amax pass then the 2D + SR pass on the same tensor, back to back")
     del wd, pr, pc, ts
 
     # 16384x8192 bf16 heavy-tailed qdq with SR + EF (residual in place), seed 7 step 123

@@ -51,7 +51,12 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
   __shared__ uint4 stage[k2dTiles * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (bank spread)
   __shared__ uint2 colbuf[COL ? k2dThreads * kColStride : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
-  const int64_t sg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - sg * ncolg;
+  // Strip groups are taken from the bottom of the tensor up: the per-tensor
+  // amax pass that precedes this one streams the tensor top to bottom, so
+  // its most recently read (last-level-cache resident) rows come first here.
+  const int64_t nsg = (M / 16 + kStrips - 1) / kStrips;
+  const int64_t rsg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - rsg * ncolg;
+  const int64_t sg = nsg - 1 - rsg;
   const int64_t col0 = cg * k2dThreads + 16 * t;
   const bool active = col0 < K;  // uniform over the 16 lanes of a tile
   const int64_t nstrips_total = M / 16;

@@ -48,6 +48,8 @@ constexpr int k46TileThreads = 512, k46TileStrips = 16;
 // takes work items x * ceil(n / 8) + 0, 1, 2, ... in dispatch order, so
 // neighbouring items (which write the two halves of shared output lines)
 // run in one L2.  Indices >= n are padding: such a workgroup exits at once.
+// The kernels map item w to n - 1 - w, so the rows the per-tensor amax pass
+// (top to bottom) read last, still in the last-level cache, are read first.
 static int64_t xcd_grid(int64_t n) { return 8 * ((n + 7) / 8); }
 NV_DEV int64_t xcd_work_index(int64_t n) {
   return (int64_t)(blockIdx.x & 7u) * ((n + 7) / 8) + (int64_t)(blockIdx.x >> 3);
@@ -189,7 +191,9 @@ __global__ __launch_bounds__(NT) void k_rowcol(
   const int64_t nwork = ncolg * ((M / 16 + STR - 1) / STR);
   const int64_t w = xcd_work_index(nwork);
   if (w >= nwork) return;  // grid padding (uniform over the workgroup)
-  const int64_t sg = w / ncolg, cg = w - sg * ncolg;
+  // work items run from the bottom of the tensor up (see xcd_work_index)
+  const int64_t wr = nwork - 1 - w;
+  const int64_t sg = wr / ncolg, cg = wr - sg * ncolg;
   const int64_t col0 = cg * NT + 16 * t;
   const bool active = col0 < K;  // uniform over the 16 lanes of a tile
   const int64_t nstrips = M / 16;
@@ -254,7 +258,9 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
   const int64_t nwork = ncolg * ((M / 16 + STR - 1) / STR);
   const int64_t w = xcd_work_index(nwork);
   if (w >= nwork) return;  // grid padding (uniform over the workgroup)
-  const int64_t sg = w / ncolg, cg = w - sg * ncolg;
+  // work items run from the bottom of the tensor up (see xcd_work_index)
+  const int64_t wr = nwork - 1 - w;
+  const int64_t sg = wr / ncolg, cg = wr - sg * ncolg;
   const int64_t col0 = cg * NT + 16 * t;
   const bool active = col0 < K;
   const int64_t nstrips = M / 16;

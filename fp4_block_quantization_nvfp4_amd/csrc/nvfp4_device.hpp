@@ -171,20 +171,21 @@ NV_DEV float div_guarded(float n, float D, float rD) {
 }
 
 // ------------------------------------------------- hardware conversions
-// gfx950 fp32 -> e2m1 (two values, round-to-nearest-even, saturating at
-// +-6; scale operand 1.0 means no scaling) into byte SEL of c.  Equal to the
-// software encoder for every finite and infinite input; a negative NaN gives
-// 0xF instead of 0x7, so callers keep NaN inputs off this path.
 // A 32-bit register whose starting contents do not matter: the empty asm
 // statement emits no instruction and only marks the register as written.
-// Code words whose four bytes are all written by hw_fp4_pair<0..3> start
-// from it, so no register clear is issued per word.
+// Code words whose four bytes are all written by hw_fp4_pair<0..3>, and
+// conversions whose unwritten bytes are masked off (hw_e4m3_pair), start
+// from it, so no register clear is issued for them.
 NV_DEV uint32_t any_u32() {
   uint32_t v;
   asm volatile("" : "=v"(v));
   return v;
 }
 
+// gfx950 fp32 -> e2m1 (two values, round-to-nearest-even, saturating at
+// +-6; scale operand 1.0 means no scaling) into byte SEL of c.  Equal to the
+// software encoder for every finite and infinite input; a negative NaN gives
+// 0xF instead of 0x7, so callers keep NaN inputs off this path.
 template <int SEL>
 NV_DEV uint32_t hw_fp4_pair(uint32_t c, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, a, b, 1.0f, SEL);
@@ -195,8 +196,11 @@ typedef unsigned int nv_u32x2 __attribute__((ext_vector_type(2)));
 typedef float nv_f32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming (nontemporal) stores for outputs a kernel writes once and never
-// reads back: the lines are not retained in the caches, which speeds up the
-// write stream of these HBM-bound kernels.
+// reads back: the lines are not retained in the caches.  They measure faster
+// for the four-over-six row kernels and the bf16-input 1x16 kernel, and
+// slower for the strip-walking 2D and row + column kernels (whose 8-byte
+// pieces of a line come from different instructions), which keep plain
+// stores.
 NV_DEV void st_nt_u8(uint8_t* p, uint32_t v) { __builtin_nontemporal_store((uint8_t)v, p); }
 NV_DEV void st_nt_u16(uint16_t* p, uint32_t v) { __builtin_nontemporal_store((uint16_t)v, p); }
 NV_DEV void st_nt_u2(void* p, uint32_t a, uint32_t b) {

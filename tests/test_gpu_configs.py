@@ -137,6 +137,18 @@ def test_act_rows_four_over_six_full_size(err):
     assert_bitwise(to_np(s2)[rows], ws, "scales (amax given)")
 
 
+def test_act_rows_four_over_six_every_row():
+    """The metric workload (8192x7168 bf16, row amax computed in the pass,
+    MAE, bound 256) against the oracle on every row, not a sample."""
+    x = _input("act_rows_input")
+    p, s, A = nv.quantize_4over6(to_dev(x), None, err_mode="mae", e4m3_scale_bound=256, row_scaled=True)
+    wA = oracle.amax(x, mode="row")
+    assert_bitwise(to_np(A), wA, "row amax")
+    wp, ws = oracle.quantize_4over6(x, wA, err_mode="mae", bound=256.0)
+    assert_bitwise(to_np(s), ws, "scales (every row)")
+    assert_bitwise(to_np(p), wp, "codes (every row)")
+
+
 def _weight_2d():
     x = _input("weight_2d_input")
     xd = to_dev(x)

@@ -12,6 +12,8 @@ import glob
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -36,19 +38,35 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, "-I", os.path.join(os.path.dirname(HERE), "include"), "-o", tmp, *sources()]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature name; that warning is expected
     err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{res.stderr}")
     if err and verbose:
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Compile every source to an object in parallel, then link the shared
+    library; the result replaces LIB atomically."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    inc = ["-I", os.path.join(os.path.dirname(HERE), "include")]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="nvfp4_build_") as tmpd:
+        objs, cmds = [], []
+        for src in sources():
+            obj = os.path.join(tmpd, os.path.basename(src) + ".o")
+            objs.append(obj)
+            cmds.append([hipcc, *compile_flags, *inc, "-c", "-o", obj, src])
+        with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

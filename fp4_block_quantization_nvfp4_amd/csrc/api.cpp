@@ -199,4 +199,19 @@ nvfp4_status nvfp4_quantize_4over6_2d(const void* x, nvfp4_dtype dt, int64_t M, 
                                             tile_scales, stream));
 }
 
+nvfp4_status nvfp4_selftest_scan(int kind, uint32_t param, uint64_t first, uint64_t count,
+                                 int chunk_log2, uint32_t* records, void* stream) {
+  if (kind < 0 || kind > 4) return NVFP4_E_ARG;
+  if (chunk_log2 < 0 || chunk_log2 > 24) return NVFP4_E_ARG;
+  const uint64_t kPatterns = uint64_t(1) << 32;
+  if (first > kPatterns || count > kPatterns - first) return NVFP4_E_RANGE;
+  if ((kind == 3 || kind == 4) && first + count > 256) return NVFP4_E_RANGE;
+  if (count == 0) return NVFP4_OK;
+  const uint64_t nchunks = (count + (uint64_t(1) << chunk_log2) - 1) >> chunk_log2;
+  if (nchunks > (uint64_t(1) << 22)) return NVFP4_E_ARG;
+  if (!records) return NVFP4_E_NULL;
+  if (!aligned(records, 16)) return NVFP4_E_ALIGN;
+  return hip_status(nvfp4::launch_selftest_scan(kind, param, first, count, chunk_log2, records, stream));
+}
+
 }  // extern "C"

@@ -91,8 +91,8 @@ __global__ __launch_bounds__(k46MaxThreads) void k_4over6(const InT* __restrict_
 // above, with exact rewrites of the per-element work:
 //  * e2m1 encode by the gfx950 packed fp32 -> fp4 conversion (scale 1.0),
 //    which rounds to nearest-even and saturates at +-6 exactly like the
-//    software encoder for every finite and infinite input (checked on all
-//    2^32 fp32 values); the block scale bytes come from the hardware
+//    software encoder for every finite and infinite input (an exhaustive
+//    scan of all fp32 patterns); the block scale bytes come from the hardware
 //    fp32 -> e4m3 conversion, equal to the software encoder on [0, 448].
 //  * The candidate choice is certified from error sums in the scaled
 //    domain (fos_block); only undecided blocks compute the per-element

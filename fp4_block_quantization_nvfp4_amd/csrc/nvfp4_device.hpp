@@ -152,10 +152,14 @@ NV_DEV void store16_bf16(uint16_t* p, const float x[16]) {
 }
 
 // ------------------------------------------------------------ divisions
-// n / D by reciprocal multiply plus one exact FMA remainder correction.
-// For D in {6, 1536, 2688} this equals the correctly rounded quotient for
-// every float32 numerator of magnitude >= 2^-117 (exponent field 10..254);
-// the host test suite proves it by exhausting all float32 numerators.
+// n / D by a precomputed reciprocal plus one exact FMA remainder correction:
+// q0 = n * fl(1/D), r = fma(-q0, D, n), q = fma(r, fl(1/D), q0), the
+// division by a divisor known in advance of Brisebarre, Muller and Raina
+// ("Accelerating correctly rounded floating-point division when the divisor
+// is known in advance", IEEE Trans. Computers 53(8), 2004).  For D in
+// {6, 1536, 2688} it equals the correctly rounded quotient for every float32
+// numerator of magnitude >= 2^-117 (exponent field 10..254); the host test
+// suite proves it by exhausting all float32 numerators.
 NV_DEV float div_fast(float n, float D, float rD) {
   const float q0 = n * rD;
   const float rem = __builtin_fmaf(-q0, D, n);
@@ -183,9 +187,12 @@ NV_DEV uint32_t any_u32() {
 }
 
 // gfx950 fp32 -> e2m1 (two values, round-to-nearest-even, saturating at
-// +-6; scale operand 1.0 means no scaling) into byte SEL of c.  Equal to the
-// software encoder for every finite and infinite input; a negative NaN gives
-// 0xF instead of 0x7, so callers keep NaN inputs off this path.
+// +-6; scale operand 1.0 means no scaling) into byte SEL of c; the other
+// bytes of c are kept.  Equal to the software encoder for every finite and
+// infinite input, in every byte position and slot (an exhaustive scan of all
+// fp32 patterns through nvfp4_selftest_scan is part of the GPU tests); a
+// negative NaN gives 0xF instead of 0x7, so callers keep NaN inputs off this
+// path.
 template <int SEL>
 NV_DEV uint32_t hw_fp4_pair(uint32_t c, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, a, b, 1.0f, SEL);
@@ -230,8 +237,8 @@ NV_DEV nv_f2 hw_fp4_values(uint32_t c) {
 // one seed for both slots: it rounds |v| up iff floor(f * 2^22) + R >= 2^22,
 // f the fractional distance between the two grid points, R the top 22 bits
 // of the seed for the first slot and of the seed shifted left by one for the
-// second (fitted on the hardware and checked on boundary cases in every
-// binade).  A seed (~u << 16) | 0xFFFF (first slot) or (~u << 15) | 0x7FFF
+// second (fitted on the hardware; the exhaustive scan of every non-NaN fp32
+// input under 44 fixed draws, each byte position and slot, confirms it).  A seed (~u << 16) | 0xFFFF (first slot) or (~u << 15) | 0x7FFF
 // (second slot) turns that into u * 2^-16 < f22, the library's rule, so the
 // pair is converted twice, once per seed, and the two nibbles are merged.
 // The converted byte lands in byte SEL of the result; the builtin does not
@@ -261,13 +268,14 @@ NV_DEV uint32_t hw_fp4_sr_word(const float* x, float rho, const uint32_t* nw) {
 }
 
 // gfx950 fp32 -> e4m3 of two scales in [0, 448] (bytes 0 and 1): equal to
-// e4m3_encode on every float32 in that range (checked exhaustively).
+// e4m3_encode on every float32 in that range, in both slots (exhaustive scan
+// of every non-negative fp32 after the 448 cap).
 NV_DEV uint32_t hw_e4m3_pair(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)any_u32(), false) & 0xFFFFu;
 }
 
 // gfx950 e4m3 byte SEL of c -> fp32: equal to e4m3_decode on every code
-// 0x00..0x7E (checked exhaustively).
+// 0x00..0x7E (all codes checked, both byte positions the kernels use).
 template <int SEL>
 NV_DEV float hw_e4m3_value(uint32_t c) {
   return __builtin_amdgcn_cvt_f32_fp8((int)c, SEL);

@@ -227,6 +227,34 @@ nvfp4_status nvfp4_quantize_4over6_2d(const void* x, nvfp4_dtype dt, int64_t M, 
                                       uint8_t* packed_row, uint8_t* packed_col,
                                       uint8_t* tile_scales, void* stream);
 
+/*
+ * Test support (not part of the quantization path).
+ *
+ * nvfp4_selftest_scan - exhaustive scan of one of the gfx950 conversions the
+ * kernels use, through the same device helpers and operand placement, so a
+ * test can compare every input pattern with the CPU oracle (the pages fix
+ * what must be matched: satfinite round-to-nearest-even e2m1 and e4m3 casts,
+ * four-over-six pull request, CuTe DSL kernel Design; stochastic rounding
+ * with probability equal to the fractional distance, fp4-train card, Method).
+ *   kind 0  fp32 -> e2m1 round-to-nearest of pattern p, param = SEL | slot << 2
+ *           (byte SEL of the word, element a or b; the other element 0, the
+ *           other bytes of the word 0xA5): y = the whole 32-bit word.
+ *   kind 1  e4m3 scale byte of min(p, 448), param = slot (0 or 1): y = byte.
+ *   kind 2  stochastic fp32 -> e2m1, param = u16 | SEL << 16 | slot << 18:
+ *           the element in `slot` takes the 16-bit draw u16: y = byte SEL.
+ *   kind 3  e2m1 byte p -> fp32 bits of element `half`, param = SEL | half << 2.
+ *   kind 4  e4m3 code p -> fp32 bits, param = SEL (0 or 1).
+ * Patterns first .. first + count - 1 (first + count <= 2^32; <= 256 for
+ * kinds 3 and 4) are cut into chunks of 2^chunk_log2 (chunk_log2 0..24, at
+ * most 2^22 chunks); records receives four uint32 per chunk (device memory,
+ * 16-byte aligned): {y(first pattern), y(last pattern), number of patterns
+ * p of the chunk with y(p) != y(p - 1), the first such p}.  Errors as for
+ * the other entry points (NVFP4_E_ARG for a bad kind or chunk size,
+ * NVFP4_E_RANGE for a run outside the pattern space).
+ */
+nvfp4_status nvfp4_selftest_scan(int kind, uint32_t param, uint64_t first, uint64_t count,
+                                 int chunk_log2, uint32_t* records, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

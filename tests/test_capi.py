@@ -101,3 +101,17 @@ def test_other_entry_points_reject():
     assert lib.nvfp4_amax(A, L.BF16, 1024, 1024, None, 1, A, A, need - 1, None) == L.E_ARG
     assert lib.nvfp4_amax(A, L.BF16, 1024, 1024, None, 1, A, None, need, None) == L.E_NULL
     assert lib.nvfp4_amax(A, L.BF16, 1024, 1024, None, 0, A, A, need, None) == L.E_ARG
+
+
+def test_selftest_scan_rejects():
+    s = L.lib().nvfp4_selftest_scan
+    assert s(5, 0, 0, 16, 4, A, None) == L.E_ARG            # unknown kind
+    assert s(-1, 0, 0, 16, 4, A, None) == L.E_ARG
+    assert s(0, 0, 0, 16, 25, A, None) == L.E_ARG           # chunk too large
+    assert s(0, 0, 0, 1 << 32, 8, A, None) == L.E_ARG       # 2^24 chunks > 2^22
+    assert s(0, 0, 1, 1 << 32, 16, A, None) == L.E_RANGE    # past the pattern space
+    assert s(0, 0, (1 << 32) + 1, 0, 16, A, None) == L.E_RANGE
+    assert s(3, 0, 0, 257, 0, A, None) == L.E_RANGE         # decodes take bytes only
+    assert s(0, 0, 0, 16, 4, None, None) == L.E_NULL
+    assert s(0, 0, 0, 16, 4, A + 8, None) == L.E_ALIGN
+    assert s(0, 0, 0, 0, 4, None, None) == L.OK             # empty run

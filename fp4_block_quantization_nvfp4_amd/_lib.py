@@ -33,6 +33,7 @@ SIGNATURES = {
     "nvfp4_quantize_rowcol": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp]),
     "nvfp4_quantize_4over6_2d": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _f32, _vp, _vp, _vp, _vp]),
     "nvfp4_selftest_scan": (_i32, [_i32, _u32, _c.c_uint64, _c.c_uint64, _i32, _vp, _vp]),
+    "nvfp4_selftest_launch_plan": (_i32, [_i32, _i64, _i64, _i32, _i32, _vp]),
 }
 
 

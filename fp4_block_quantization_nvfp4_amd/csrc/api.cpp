@@ -5,6 +5,7 @@
 
 #include "../../include/nvfp4.h"
 #include "nvfp4_launch.hpp"
+#include "nvfp4_plan.hpp"
 
 namespace {
 
@@ -212,6 +213,29 @@ nvfp4_status nvfp4_selftest_scan(int kind, uint32_t param, uint64_t first, uint6
   if (!records) return NVFP4_E_NULL;
   if (!aligned(records, 16)) return NVFP4_E_ALIGN;
   return hip_status(nvfp4::launch_selftest_scan(kind, param, first, count, chunk_log2, records, stream));
+}
+
+nvfp4_status nvfp4_selftest_launch_plan(int entry, int64_t M, int64_t K, int in_bf16, int variant,
+                                        int64_t* plan) {
+  if (entry < 0 || entry > 6) return NVFP4_E_ARG;
+  const bool tiles = entry == 3 || entry == 4 || entry == 5 || (entry == 1 && variant == 1);
+  if (nvfp4_status st = check_shape(M, K, tiles)) return st;
+  if (!plan) return NVFP4_E_NULL;
+  nvfp4::LaunchPlan p{};
+  switch (entry) {
+    case 0: p = nvfp4::plan_quant1x16(M, K); break;
+    case 1: p = nvfp4::plan_dequant(M, K); break;
+    case 2: p = nvfp4::plan_4over6(in_bf16 != 0, M, K); break;
+    case 3: p = nvfp4::plan_quant2d(M, K); break;
+    case 4: p = nvfp4::plan_rowcol(M, K, variant != 0); break;
+    case 5: p = nvfp4::plan_4over6_2d(M, K); break;
+    default: p = nvfp4::plan_amax(M, K, variant != 0); break;
+  }
+  plan[0] = p.kernel;
+  plan[1] = p.launches;
+  plan[2] = p.grid;
+  plan[3] = p.block;
+  return NVFP4_OK;
 }
 
 }  // extern "C"

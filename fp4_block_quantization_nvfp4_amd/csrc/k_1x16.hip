@@ -23,10 +23,9 @@
 // MFMA.
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
+#include "nvfp4_plan.hpp"
 
 namespace nvfp4 {
-
-constexpr int kThreads = 256;
 
 // Max over the four lanes of a quad (every lane of the quad gets it).
 NV_DEV uint32_t quad_max_u32(uint32_t v) {
@@ -191,7 +190,8 @@ template <typename InT, bool HAS_RES, bool SR, bool GLOBAL>
 static int dispatch_out(const InT* x, float* res, const float* ga, uint32_t key, int64_t ng,
                         uint8_t* packed, uint8_t* scales, void* out, int out_kind,
                         hipStream_t st) {
-  const dim3 grid((unsigned)((ng + kThreads - 1) / kThreads)), block(kThreads);
+  const LaunchPlan pl = plan_quant1x16(ng, 4);  // ng = M*K/4 four-element groups
+  const dim3 grid((unsigned)pl.grid), block(pl.block);
   const bool codes = packed != nullptr;
   if (out_kind == 0)
     hipLaunchKernelGGL((k_quant1x16<InT, HAS_RES, SR, GLOBAL, 0, true>), grid, block, 0, st,
@@ -278,7 +278,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
 template <int SMODE, bool TILE16>
 static int dq_out(const uint8_t* p, const uint8_t* s, const float* ga, float D, int64_t nbk,
                   int64_t ng, void* out, int out_bf16, hipStream_t st) {
-  const dim3 grid((unsigned)((ng + kThreads - 1) / kThreads)), block(kThreads);
+  const LaunchPlan pl = plan_dequant(ng, 4);  // ng = M*K/4 four-element groups
+  const dim3 grid((unsigned)pl.grid), block(pl.block);
   if (out_bf16)
     hipLaunchKernelGGL((k_dequant<SMODE, TILE16, true>), grid, block, 0, st, p, s, ga, D, nbk, ng, out);
   else

@@ -21,10 +21,10 @@
 // into a per-column buffer that is written out once per workgroup.
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
+#include "nvfp4_plan.hpp"
 
 namespace nvfp4 {
 
-constexpr int k2dThreads = 512;            // lanes per workgroup = columns covered (16 per tile)
 constexpr int k2dTiles = k2dThreads / 16;   // tiles side by side
 
 // Max over the 16 lanes of a DPP row (every lane of the row gets it): two
@@ -40,7 +40,6 @@ NV_DEV uint32_t row16_max_u32(uint32_t v) {
   return o > v ? o : v;
 }
 
-constexpr int kStrips = 16;         // 16-row strips per workgroup (256 rows)
 constexpr int kColStride = kStrips + 1;  // uint2 per column in the column buffer (+1 spreads banks)
 
 template <typename InT, bool SR, bool GLOBAL, bool COL, bool UP>
@@ -208,9 +207,9 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
 template <typename InT, bool SR, bool GLOBAL, bool UP>
 static int launch2d_col(const InT* x, const float* ga, uint32_t key, int64_t M, int64_t K,
                         uint8_t* pr, uint8_t* pc, uint8_t* ts, hipStream_t st) {
-  const int64_t ncolg = (K + k2dThreads - 1) / k2dThreads;
-  const int64_t nsg = (M / 16 + kStrips - 1) / kStrips;
-  const dim3 grid((unsigned)(ncolg * nsg)), block(k2dThreads);
+  const int64_t ncolg = quant2d_colgroups(K);
+  const LaunchPlan pl = plan_quant2d(M, K);
+  const dim3 grid((unsigned)pl.grid), block(pl.block);
   if (pc) hipLaunchKernelGGL((k_quant2d<InT, SR, GLOBAL, true, UP>), grid, block, 0, st, x, ga, key, M, K, pr, pc, ts, ncolg);
   else hipLaunchKernelGGL((k_quant2d<InT, SR, GLOBAL, false, UP>), grid, block, 0, st, x, ga, key, M, K, pr, pc, ts, ncolg);
   return (int)hipGetLastError();

@@ -23,10 +23,9 @@
 #include "nvfp4_device.hpp"
 #include "nvfp4_fos.hpp"
 #include "nvfp4_launch.hpp"
+#include "nvfp4_plan.hpp"
 
 namespace nvfp4 {
-
-constexpr int k46MaxThreads = 1024;
 
 NV_DEV float wave_max46(float v) {
 #pragma unroll
@@ -163,7 +162,6 @@ NV_DEV uint32_t wave_max_pk_u16(uint32_t v) {
 
 // One workgroup of kRowThreads lanes (two waves) per row; lane t owns blocks
 // t, t + kRowThreads, ... (R per lane).
-constexpr int kRowThreads = 128;
 
 template <bool MSE, int MODE, int R>
 __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __restrict__ x,
@@ -253,28 +251,38 @@ __global__ __launch_bounds__(kRowThreads) void k_4over6_rows(const uint16_t* __r
   }
 }
 
+// One launch per chunk of at most kRowChunk rows (grid x workgroup stays far
+// below 2^32 work-items); a chunk's pointers start at its first row.
 template <bool MSE, int MODE>
 static int launch_rows_R(int R, const uint16_t* x, float* amax, float D, int64_t M, int64_t K,
                          uint8_t* packed, uint8_t* scales, hipStream_t st) {
-  const dim3 grid((unsigned)M), block(kRowThreads);
+  const LaunchPlan pl = plan_4over6(1, M, K);
+  for (int64_t l = 0; l < pl.launches; ++l) {
+    const int64_t m0 = l * kRowChunk, rows = (M - m0) < kRowChunk ? (M - m0) : kRowChunk;
+    const uint16_t* xc = x + m0 * K;
+    float* ac = MODE == 1 ? amax : amax + m0;
+    uint8_t* pc = packed + m0 * (K / 2);
+    uint8_t* sc = scales + m0 * (K / 16);
+    const dim3 grid((unsigned)rows), block(pl.block);
 #define NV46_CASE(RR) \
-  case RR: hipLaunchKernelGGL((k_4over6_rows<MSE, MODE, RR>), grid, block, 0, st, x, amax, D, M, K, packed, scales); break;
-  switch (R) {
-    NV46_CASE(1) NV46_CASE(2) NV46_CASE(3) NV46_CASE(4) NV46_CASE(5) NV46_CASE(6) NV46_CASE(7) NV46_CASE(8)
-    default: return (int)hipErrorInvalidValue;
-  }
+  case RR: hipLaunchKernelGGL((k_4over6_rows<MSE, MODE, RR>), grid, block, 0, st, xc, ac, D, rows, K, pc, sc); break;
+    switch (R) {
+      NV46_CASE(1) NV46_CASE(2) NV46_CASE(3) NV46_CASE(4) NV46_CASE(5) NV46_CASE(6) NV46_CASE(7) NV46_CASE(8)
+      default: return (int)hipErrorInvalidValue;
+    }
 #undef NV46_CASE
-  return (int)hipGetLastError();
+    const int e = (int)hipGetLastError();
+    if (e) return e;
+  }
+  return 0;
 }
 
 template <typename InT, bool MSE>
 static int launch46_mode(const InT* x, float* amax, int mode, int amax_is_input, float D,
                          int64_t M, int64_t K, uint8_t* packed, uint8_t* scales, hipStream_t st) {
-  const int64_t nbk = K / 16;
-  int threads = (int)((nbk + 63) / 64 * 64);
-  if (threads > k46MaxThreads) threads = k46MaxThreads;
-  if (threads < 64) threads = 64;
-  const unsigned grid = (unsigned)(M < 1048576 ? M : 1048576);
+  const LaunchPlan pl = plan_4over6(sizeof(InT) == 2, M, K);
+  const int threads = pl.block;
+  const unsigned grid = (unsigned)pl.grid;
   if (mode == 1)
     hipLaunchKernelGGL((k_4over6<InT, MSE, 1>), dim3(grid), dim3(threads), 0, st, x, amax, D, M, K, packed, scales);
   else if (amax_is_input)
@@ -291,7 +299,7 @@ int launch_4over6(const void* x, int in_bf16, int64_t M, int64_t K, float* amax,
   const float D = 6.0f * bound;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int64_t nbk = K / 16;
-  if (in_bf16 && nbk <= kRowThreads * 8 && M <= 0x7FFFFFFF) {
+  if (use_rows_kernel(in_bf16, K)) {
     const int R = (int)((nbk + kRowThreads - 1) / kRowThreads);
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
     const int md = mode == 1 ? 1 : (amax_is_input ? 2 : 3);
@@ -304,7 +312,7 @@ int launch_4over6(const void* x, int in_bf16, int64_t M, int64_t K, float* amax,
     if (md == 2) return launch_rows_R<false, 2>(R, xb, amax, D, M, K, packed, scales, st);
     return launch_rows_R<false, 3>(R, xb, amax, D, M, K, packed, scales, st);
   }
-  if (in_bf16) {
+  if (in_bf16) {  // rows longer than the row kernel takes
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
     return mse ? launch46_mode<uint16_t, true>(xb, amax, mode, amax_is_input, D, M, K, packed, scales, st)
                : launch46_mode<uint16_t, false>(xb, amax, mode, amax_is_input, D, M, K, packed, scales, st);

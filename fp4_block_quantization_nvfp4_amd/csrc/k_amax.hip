@@ -12,11 +12,10 @@
 // row, same reductions.
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
+#include "nvfp4_plan.hpp"
 
 namespace nvfp4 {
 
-constexpr int kAmaxThreads = 256;
-constexpr int kAmaxMaxGroups = 2048;
 
 NV_DEV float wave_max(float v) {
 #pragma unroll
@@ -100,16 +99,8 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_rows(const InT* __restric
   }
 }
 
-static int64_t partial_groups(int64_t M, int64_t K) {
-  const int64_t ng = M * K / 16;
-  int64_t g = (ng + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
-  if (g < 1) g = 1;
-  if (g > kAmaxMaxGroups) g = kAmaxMaxGroups;
-  return g;
-}
-
 size_t amax_workspace_bytes(int64_t M, int64_t K) {
-  return (size_t)partial_groups(M, K) * sizeof(float);
+  return (size_t)amax_partial_groups(M, K) * sizeof(float);
 }
 
 template <typename InT>
@@ -118,12 +109,12 @@ static int amax_typed(const InT* x, int64_t M, int64_t K, const float* res, int 
   const int64_t ng = M * K / 16;
   if (mode == 2) {
     if (M == 0) return 0;
-    const unsigned grid = (unsigned)(M < 65536 ? M : 65536);
+    const unsigned grid = (unsigned)plan_amax(M, K, 1).grid;
     if (res) hipLaunchKernelGGL((k_amax_rows<InT, true>), dim3(grid), dim3(kAmaxThreads), 0, st, x, res, M, K, out);
     else hipLaunchKernelGGL((k_amax_rows<InT, false>), dim3(grid), dim3(kAmaxThreads), 0, st, x, res, M, K, out);
     return (int)hipGetLastError();
   }
-  const int64_t groups = partial_groups(M, K);
+  const int64_t groups = plan_amax(M, K, 0).grid;
   if (ng > 0) {
     if (res) hipLaunchKernelGGL((k_amax_partial<InT, true>), dim3((unsigned)groups), dim3(kAmaxThreads), 0, st, x, res, ng, ws);
     else hipLaunchKernelGGL((k_amax_partial<InT, false>), dim3((unsigned)groups), dim3(kAmaxThreads), 0, st, x, res, ng, ws);

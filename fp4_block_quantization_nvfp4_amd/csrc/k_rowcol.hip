@@ -33,15 +33,15 @@
 #include "nvfp4_device.hpp"
 #include "nvfp4_fos.hpp"
 #include "nvfp4_launch.hpp"
+#include "nvfp4_plan.hpp"
 
 namespace nvfp4 {
 
-// Workgroup shapes (lanes = columns covered, 16-row strips per workgroup).
-// The four-over-six row + column pass is VALU-heavy and gains from more
-// resident workgroups (128 columns: half the LDS); the standard pass is
-// bound by its memory pattern and prefers 256-byte row segments.
-constexpr int kRowColThreads = 256, kRowColFosThreads = 128, kRowColStrips = 16;
-constexpr int k46TileThreads = 512, k46TileStrips = 16;
+// Workgroup shapes (nvfp4_plan.hpp: lanes = columns covered, 16-row strips
+// per workgroup).  The four-over-six row + column pass is VALU-heavy and
+// gains from more resident workgroups (128 columns: half the LDS); the
+// standard pass is bound by its memory pattern and prefers 256-byte row
+// segments.
 
 // XCD-aware work order.  The dispatcher hands workgroup i to XCD i % 8, and
 // each XCD has its own L2.  With a grid of xcd_grid(n) workgroups, XCD x
@@ -50,7 +50,6 @@ constexpr int k46TileThreads = 512, k46TileStrips = 16;
 // run in one L2.  Indices >= n are padding: such a workgroup exits at once.
 // The kernels map item w to n - 1 - w, so the rows the per-tensor amax pass
 // (top to bottom) read last, still in the last-level cache, are read first.
-static int64_t xcd_grid(int64_t n) { return 8 * ((n + 7) / 8); }
 NV_DEV int64_t xcd_work_index(int64_t n) {
   return (int64_t)(blockIdx.x & 7u) * ((n + 7) / 8) + (int64_t)(blockIdx.x >> 3);
 }
@@ -366,12 +365,6 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
   if (COL) flush_columns<NT, STR>(colbuf, nullptr, cg, sg, nst, M, K, packed_col, nullptr);
 }
 
-template <int NT, int STR>
-static dim3 rc_grid(int64_t M, int64_t K, int64_t& ncolg) {
-  ncolg = (K + NT - 1) / NT;
-  const int64_t nsg = (M / 16 + STR - 1) / STR;
-  return dim3((unsigned)xcd_grid(ncolg * nsg));
-}
 
 template <typename InT>
 static int launch_rowcol_t(const InT* x, const float* ga, int fos, int mse, float D, int64_t M,
@@ -379,13 +372,15 @@ static int launch_rowcol_t(const InT* x, const float* ga, int fos, int mse, floa
                            hipStream_t st) {
   constexpr int STR = kRowColStrips;
   int64_t ncolg;
+  const LaunchPlan pl = plan_rowcol(M, K, fos);
+  const dim3 grid((unsigned)pl.grid), block(pl.block);
   if (!fos) {
     constexpr int NT = kRowColThreads;
-    const dim3 grid = rc_grid<NT, STR>(M, K, ncolg), block(NT);
+    ncolg = ceil_div(K, NT);
     hipLaunchKernelGGL((k_rowcol<InT, false, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
   } else {
     constexpr int NT = kRowColFosThreads;
-    const dim3 grid = rc_grid<NT, STR>(M, K, ncolg), block(NT);
+    ncolg = ceil_div(K, NT);
     if (mse)
       hipLaunchKernelGGL((k_rowcol<InT, true, true, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
     else
@@ -411,8 +406,9 @@ template <typename InT, bool MSE>
 static int launch_4over6_2d_t(const InT* x, const float* ga, float D, int64_t M, int64_t K,
                               uint8_t* pr, uint8_t* pc, uint8_t* ts, hipStream_t st) {
   constexpr int NT = k46TileThreads, STR = k46TileStrips;
-  int64_t ncolg;
-  const dim3 grid = rc_grid<NT, STR>(M, K, ncolg), block(NT);
+  const int64_t ncolg = ceil_div(K, NT);
+  const LaunchPlan pl = plan_4over6_2d(M, K);
+  const dim3 grid((unsigned)pl.grid), block(pl.block);
   if (pc) hipLaunchKernelGGL((k_4over6_2d<InT, MSE, true, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg);
   else hipLaunchKernelGGL((k_4over6_2d<InT, MSE, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg);
   return (int)hipGetLastError();

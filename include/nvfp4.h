@@ -255,6 +255,23 @@ nvfp4_status nvfp4_quantize_4over6_2d(const void* x, nvfp4_dtype dt, int64_t M, 
 nvfp4_status nvfp4_selftest_scan(int kind, uint32_t param, uint64_t first, uint64_t count,
                                  int chunk_log2, uint32_t* records, void* stream);
 
+/*
+ * nvfp4_selftest_launch_plan - the launch geometry an entry point would use
+ * for an [M, K] tensor, computed by the same host functions as the launchers
+ * (no device work, no GPU needed), so a host test can check every accepted
+ * shape against the dispatch limits.
+ *   entry    0 quantize / qdq, 1 dequantize (variant 1: 16x16 tiles),
+ *            2 quantize_4over6, 3 quantize_2d, 4 quantize_rowcol (variant 1:
+ *            four-over-six), 5 quantize_4over6_2d, 6 amax (variant 1: per row;
+ *            for per tensor the plan is the partial pass).
+ *   in_bf16  input dtype (it selects the four-over-six kernel).
+ *   plan     HOST pointer to four int64: {kernel id, launches, workgroups of
+ *            the largest launch, lanes per workgroup}.
+ * Shapes are validated as by the entry point (NVFP4_E_SHAPE, NVFP4_E_RANGE).
+ */
+nvfp4_status nvfp4_selftest_launch_plan(int entry, int64_t M, int64_t K, int in_bf16, int variant,
+                                        int64_t* plan);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,5 +1,5 @@
 """Host-side logic of bench.py (no GPU): the one-GPU guard, the reader of
-the committed HBM-traffic counter summary and the percentile helper."""
+the committed HBM-traffic counter summaries and the CPU-baseline worker."""
 import os
 import subprocess
 import sys
@@ -24,26 +24,26 @@ def _summary(tmp_path, sha, bytes_):
     return str(p)
 
 
-def test_traffic_read_only_for_the_current_kernel_source(tmp_path, monkeypatch):
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", _summary(tmp_path, bench.src_hash(), "151235333"))
-    assert bench.read_traffic(150470656) == 151235333
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", _summary(tmp_path, "0" * 16, "151235333"))
-    assert bench.read_traffic(150470656) is None
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.txt"))
-    assert bench.read_traffic(150470656) is None
+def test_traffic_read_only_for_the_current_kernel_source(tmp_path):
+    for w in bench.TRAFFIC:
+        assert bench.read_traffic(w, _summary(tmp_path, bench.src_hash(w), "151235333")) == 151235333
+        assert bench.read_traffic(w, _summary(tmp_path, "0" * 16, "151235333")) is None
+        assert bench.read_traffic(w, str(tmp_path / "absent.txt")) is None
 
 
 def test_source_hash_covers_the_kernel_and_its_headers():
-    h = bench.src_hash()
-    assert len(h) == 16 and int(h, 16) >= 0
-    assert h == bench.src_hash()
+    for w, (f, srcs) in bench.TRAFFIC.items():
+        assert f.startswith("traffic_") and f.endswith(".txt")
+        for s in srcs:
+            assert os.path.exists(os.path.join(bench.CSRC, s)), s
+        h = bench.src_hash(w)
+        assert len(h) == 16 and int(h, 16) >= 0 and h == bench.src_hash(w)
+    assert bench.METRIC in bench.TRAFFIC
 
 
-def test_percentile_is_nearest_rank():
-    v = [7.0, 1.0, 3.0, 9.0, 5.0]
-    assert bench.percentile(v, 0) == 1.0
-    assert bench.percentile(v, 50) == 5.0
-    assert bench.percentile(v, 100) == 9.0
-    assert bench.percentile(list(range(101)), 10) == 10
-    assert bench.percentile(list(range(101)), 90) == 90
-    assert bench.percentile([4.0], 90) == 4.0
+def test_cpu_baseline_worker_runs_the_oracle():
+    import numpy as np
+    import workloads
+
+    x = workloads.act_rows_input((4, 256))
+    assert bench._cpu_task(x, "mae") == 4 * 256

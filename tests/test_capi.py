@@ -115,3 +115,35 @@ def test_selftest_scan_rejects():
     assert s(0, 0, 0, 16, 4, None, None) == L.E_NULL
     assert s(0, 0, 0, 16, 4, A + 8, None) == L.E_ALIGN
     assert s(0, 0, 0, 0, 4, None, None) == L.OK             # empty run
+
+
+def _plan(entry, M, K, bf16=1, variant=0):
+    out = (ctypes.c_int64 * 4)()
+    st = L.lib().nvfp4_selftest_launch_plan(entry, M, K, bf16, variant, out)
+    return st, list(out)
+
+
+@pytest.mark.parametrize("entry,variant", [(0, 0), (1, 0), (1, 1), (2, 0), (3, 0), (4, 0), (4, 1), (5, 0),
+                                           (6, 0), (6, 1)])
+@pytest.mark.parametrize("bf16", [0, 1])
+def test_launch_geometry_within_dispatch_limits(entry, variant, bf16):
+    """Every accepted shape, down to 16-element rows with the largest M the
+    2^33-element limit allows (the case where one workgroup per row would
+    exceed 2^32 work-items), keeps each launch under 2^32 work-items and
+    2^31 workgroups and covers all rows."""
+    for K in (16, 32, 128, 320, 7168, 16384, 16400, 65536, 1 << 20, 1 << 33):
+        for M in (16, 8192, 1 << 25, (1 << 25) + 16, 1 << 26, (1 << 33) // K // 16 * 16):
+            if M * K > 1 << 33 or M < 1:
+                continue
+            st, (kern, launches, grid, block) = _plan(entry, M, K, bf16, variant)
+            assert st == L.OK, (entry, M, K)
+            assert 1 <= grid < 1 << 31 and 64 <= block <= 1024 and grid * block < 1 << 32, (entry, M, K, grid, block)
+            if kern == 2:  # the bf16 row kernel: one workgroup per row, in chunks
+                assert bf16 and K <= 16384 and launches * grid >= M and grid * (launches - 1) < M
+            else:
+                assert launches == 1
+    assert _plan(2, 1 << 26, 16)[1][:2] == [2, 4]             # 2^26 rows: four row-kernel launches
+    assert _plan(2, 8192, 7168)[1] == [2, 1, 8192, 128]      # the metric shape
+    assert _plan(2, 8192, 7168, bf16=0)[1][0] == 3           # fp32 takes the generic kernel
+    assert _plan(3, 24, 32)[0] == L.E_SHAPE and _plan(7, 16, 16)[0] == L.E_ARG
+    assert _plan(0, 1 << 22, 1 << 12)[0] == L.E_RANGE

@@ -107,3 +107,47 @@ def test_stochastic_rounding_dense_sweep():
     assert_bitwise(to_np(t2), wt, "2d tile scales")
     assert_bitwise(to_np(r2), wr, "2d rowwise")
     assert_bitwise(to_np(c2), wc, "2d columnwise")
+
+
+@pytest.mark.parametrize("seed,step", [(0, 0), (7, 123), (0xDEADBEEF, 5)])
+def test_stochastic_rounding_on_each_elements_draw_boundary(seed, step):
+    """Unit-scale blocks [6, v_1 .. v_15] where every v_i is placed from
+    element i's own draw u_i (the counter-based stream of the fp4-train
+    card, Method): its fractional distance in a grid interval is exactly
+    u_i * 2^-16 (stays down), or that plus 2^-24, 2^-23 (below the 22-bit
+    truncation: stays down under the library's reading) or 2^-22 (goes up).
+    Intervals cycle over all seven, so every binade of the scaled value from
+    2^-17 to 6 sees boundary cases; quantize, qdq + residual and the 2D pass
+    are compared with the oracle."""
+    n_blocks = 1 << 14
+    M, K = n_blocks // 4, 64
+    idx = np.arange(M * K, dtype=np.int64).reshape(M, K)
+    u = oracle.sr_u16(idx, seed, step).astype(np.float64)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    k = (idx // 16 + idx) % 7                           # interval [grid[k], grid[k+1])
+    delta = np.array([0.0, 2.0 ** -24, 2.0 ** -23, 2.0 ** -22])[(idx // 7) % 4]
+    v = grid[k] + (u / 65536.0 + delta) * (grid[k + 1] - grid[k])
+    # an offset finer than the fp32 spacing of its interval becomes 2^-22
+    fine = v.astype(np.float32).astype(np.float64) != v
+    v = np.where(fine, grid[k] + (u / 65536.0 + 2.0 ** -22) * (grid[k + 1] - grid[k]), v)
+    x = v.astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), v)   # every v is exact in fp32
+    x = np.where((idx // 3) % 2 == 1, -x, x).astype(np.float32)
+    x[:, ::16] = 6.0                                   # block amax 6: scale 1, rho 1
+    xd = to_dev(x)
+    wp, ws = oracle.quantize(x, stochastic=True, seed=seed, step=step)
+    p, s = nv.quantize(xd, stochastic=True, seed=seed, step=step)
+    assert np.all(ws == 0x38)
+    assert_bitwise(to_np(s), ws, "scales")
+    assert_bitwise(to_np(p), wp, "codes")
+    r = np.zeros_like(x)
+    wo = oracle.qdq(x, stochastic=True, residual=r, seed=seed, step=step, out="f32")[0]
+    rd = torch.zeros_like(xd)
+    got = nv.qdq(xd, stochastic=True, residual=rd, seed=seed, step=step, out_dtype=torch.float32)
+    assert_bitwise(to_np(got), wo, "qdq")
+    assert_bitwise(to_np(rd), r, "residual")
+    wr, wc, wt = oracle.quantize_2d(x, stochastic=True, seed=seed, step=step)
+    r2, c2, t2 = nv.quantize_2d(xd, stochastic=True, seed=seed, step=step)
+    assert_bitwise(to_np(t2), wt, "2d tile scales")
+    assert_bitwise(to_np(r2), wr, "2d rowwise")
+    assert_bitwise(to_np(c2), wc, "2d columnwise")

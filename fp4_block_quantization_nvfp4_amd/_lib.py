@@ -25,6 +25,7 @@ SIGNATURES = {
     "nvfp4_status_str": (_c.c_char_p, [_i32]),
     "nvfp4_amax_workspace_bytes": (_sz, [_i64, _i64]),
     "nvfp4_amax": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "nvfp4_amax_noalloc": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _vp, _vp]),
     "nvfp4_quantize": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _u32, _u32, _vp, _vp, _vp]),
     "nvfp4_dequantize": (_i32, [_vp, _vp, _i64, _i64, _i32, _vp, _i32, _f32, _vp, _i32, _vp]),
     "nvfp4_qdq": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _u32, _u32, _vp, _i32, _vp, _vp, _vp]),

@@ -67,6 +67,22 @@ nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
                                        stream));
 }
 
+nvfp4_status nvfp4_amax_noalloc(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
+                                const float* residual, nvfp4_scale_mode mode, float* amax_out,
+                                void* stream) {
+  if (nvfp4_status st = check_shape(M, K, false)) return st;
+  if (!dtype_ok(dt)) return NVFP4_E_DTYPE;
+  if (mode != NVFP4_SCALE_TENSOR && mode != NVFP4_SCALE_ROW) return NVFP4_E_ARG;
+  if (!amax_out) return NVFP4_E_NULL;
+  if (M != 0 && K != 0 && !x) return NVFP4_E_NULL;
+  if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(amax_out, 4)) return NVFP4_E_ALIGN;
+  if (mode == NVFP4_SCALE_TENSOR &&
+      nvfp4::amax_partial_groups(M, K) > nvfp4::amax_noalloc_max_partials())
+    return NVFP4_E_RANGE;
+  return hip_status(nvfp4::launch_amax_noalloc(x, dt == NVFP4_BF16, M, K, residual,
+                                               mode == NVFP4_SCALE_TENSOR ? 1 : 2, amax_out, stream));
+}
+
 static nvfp4_status quant_common(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
                                  float* residual, const float* global_amax, nvfp4_round rnd,
                                  uint32_t seed, uint32_t step, uint8_t* packed, uint8_t* scales,

@@ -10,6 +10,8 @@
 // reduces the partials and writes A.  Max is exact and order-free, so the
 // result does not depend on the launch geometry.  Per row: one workgroup per
 // row, same reductions.
+#include <mutex>
+
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 #include "nvfp4_plan.hpp"
@@ -130,6 +132,55 @@ int launch_amax(const void* x, int in_bf16, int64_t M, int64_t K, const float* r
   if (in_bf16)
     return amax_typed(reinterpret_cast<const uint16_t*>(x), M, K, residual, mode, amax_out, ws, st);
   return amax_typed(reinterpret_cast<const float*>(x), M, K, residual, mode, amax_out, ws, st);
+}
+
+// ------------------------------------------------ allocation-free variant
+// The per-tensor pass keeps its per-workgroup partial maxima in this
+// file-scope device array instead of a caller's workspace.  Every GPU the
+// library runs on holds its own copy (kAmaxMaxGroups floats, 8 KiB) until
+// the process ends.  Host code never passes the array's name to a kernel (on
+// the host it only names a stand-in): the device address of the current
+// GPU's copy is looked up once per device with hipGetSymbolAddress and kept.
+// Nothing needs clearing between calls: pass 1 writes every partial that
+// pass 2 reads.  Calls that overlap on one GPU share the array and race.
+constexpr int kScratchFloats = kAmaxMaxGroups;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+// Device address of the current GPU's scratch array (nullptr and a HIP
+// error code on failure).
+static float* scratch_for_current_device(int* err) {
+  static std::mutex mu;
+  static float* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? (int)e : (int)hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? (int)e : (int)hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    ptrs[dev] = static_cast<float*>(p);
+  }
+  return ptrs[dev];
+}
+
+int64_t amax_noalloc_max_partials() { return kScratchFloats; }
+
+int launch_amax_noalloc(const void* x, int in_bf16, int64_t M, int64_t K, const float* residual,
+                        int mode, float* amax_out, void* stream) {
+  if (mode == 2) return launch_amax(x, in_bf16, M, K, residual, mode, amax_out, nullptr, stream);
+  if (amax_partial_groups(M, K) > kScratchFloats) return (int)hipErrorInvalidValue;
+  int err = 0;
+  float* ws = scratch_for_current_device(&err);
+  if (!ws) return err;
+  return launch_amax(x, in_bf16, M, K, residual, mode, amax_out, ws, stream);
 }
 
 }  // namespace nvfp4

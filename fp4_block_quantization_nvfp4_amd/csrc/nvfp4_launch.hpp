@@ -39,6 +39,12 @@ size_t amax_workspace_bytes(int64_t M, int64_t K);
 int launch_amax(const void* x, int in_bf16, int64_t M, int64_t K, const float* residual,
                 int mode, float* amax_out, void* workspace, void* stream);
 
+// Allocation-free per-tensor / per-row amax: partials in the library's own
+// device scratch array (k_amax.hip).
+int64_t amax_noalloc_max_partials();
+int launch_amax_noalloc(const void* x, int in_bf16, int64_t M, int64_t K, const float* residual,
+                        int mode, float* amax_out, void* stream);
+
 // Test support: exhaustive conversion scans (k_selftest.hip).
 int launch_selftest_scan(int kind, uint32_t param, uint64_t first, uint64_t count, int chunk_log2,
                          uint32_t* records, void* stream);

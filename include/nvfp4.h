@@ -97,6 +97,24 @@ nvfp4_status nvfp4_amax(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_amax_noalloc - nvfp4_amax for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same result, bit for bit, with no workspace
+ * argument.  The per-tensor pass keeps its per-workgroup partial maxima in a
+ * device array owned by the library (8 KiB per GPU, held until the process
+ * ends; at most 2048 partials, which every shape with M*K <= 2^33 fits:
+ * otherwise NVFP4_E_RANGE).  The array's device address is looked up on the
+ * first call on each GPU (hipGetSymbolAddress; a failure returns
+ * NVFP4_E_HIP).  The call allocates nothing.  All calls on one GPU share
+ * that array, so calls that overlap on one GPU (concurrent streams or host
+ * threads) race; serialize them.  Arguments and errors otherwise as
+ * nvfp4_amax; mode ROW uses no scratch at all.
+ */
+nvfp4_status nvfp4_amax_noalloc(const void* x, nvfp4_dtype dt, int64_t M, int64_t K,
+                                const float* residual, nvfp4_scale_mode mode, float* amax_out,
+                                void* stream);
+
+/*
  * nvfp4_quantize - NVFP4 quantize on 1x16 blocks (fp4-train, API
  * quantize(x, stochastic, residual, seed, step); Method).
  *   x        [M, K] fp32 or bf16 (dt).

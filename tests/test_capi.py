@@ -147,3 +147,14 @@ def test_launch_geometry_within_dispatch_limits(entry, variant, bf16):
     assert _plan(2, 8192, 7168, bf16=0)[1][0] == 3           # fp32 takes the generic kernel
     assert _plan(3, 24, 32)[0] == L.E_SHAPE and _plan(7, 16, 16)[0] == L.E_ARG
     assert _plan(0, 1 << 22, 1 << 12)[0] == L.E_RANGE
+
+
+def test_amax_noalloc_rejects():
+    f = L.lib().nvfp4_amax_noalloc
+    assert f(A, L.BF16, 1024, 1024, None, 0, A, None) == L.E_ARG       # mode NONE
+    assert f(A, L.BF16, 1024, 1000, None, 1, A, None) == L.E_SHAPE
+    assert f(A, 5, 1024, 1024, None, 1, A, None) == L.E_DTYPE
+    assert f(A, L.BF16, 1024, 1024, None, 1, None, None) == L.E_NULL
+    assert f(None, L.BF16, 1024, 1024, None, 1, A, None) == L.E_NULL
+    assert f(A + 4, L.BF16, 1024, 1024, None, 1, A, None) == L.E_ALIGN
+    assert f(A, L.BF16, 1 << 22, 1 << 12, None, 1, A, None) == L.E_RANGE  # M*K > 2^33

@@ -5,61 +5,191 @@
 // one pass (the fused row + column kernel the four-over-six pull request lists
 // as a follow-up), so no caller-side transpose is needed.
 //
-// Mapping: a workgroup of 512 lanes covers 512 columns and walks down up to
-// 16 strips of 16 rows (a 256 x 512 region); in each strip it holds 32 tiles
-// side by side, four per wave.  Lane (t, r) = (tid / 16, tid % 16)
-// holds row r of tile t: 16 consecutive elements read with 128-bit loads, so
-// each wave reads 16 rows x 128 contiguous bytes.  The tile amax is reduced
-// across the 16 lanes of the tile with cross-lane max (all 16 lanes of a tile
-// sit in one 16-lane row of the wave; DPP, no LDS).  Codes come from the
-// hardware fp32 -> e2m1 conversions: round-to-nearest (exact for finite
-// inputs) or stochastic rounding with one 16-bit draw per element; tiles
-// holding a NaN or an infinity use the software encoder.  The scale byte
-// comes from the exact fp32 -> e4m3 conversion.  The rowwise codes go out as
-// one 8-byte store per lane.  For the columnwise codes each lane stages its
-// 16 codes as bytes in LDS; lane (t, c) then gathers column c of its tile
-// into a per-column buffer that is written out once per workgroup.
+// Mapping: a workgroup of 512 lanes (8 waves) covers 512 columns and walks
+// down up to 16 strips of 16 rows (a 256 x 512 region).  In every strip wave w
+// owns rows 2w and 2w + 1, and lane l of a wave holds columns 8l .. 8l + 7 of
+// both rows, so one load instruction of a wave reads 1 KB (bf16) of one row:
+// long contiguous runs per row, which the memory system streams much faster
+// than 16 rows x 128 bytes.  Tile t of the strip (columns 16t .. 16t + 15) is
+// the lane pair (2t, 2t + 1) of all eight waves: the tile amax is the max over
+// the pair (one DPP swap), then over the eight waves through a small LDS
+// table (one barrier per strip; the table is double-buffered by strip
+// parity).  Codes come from the hardware fp32 -> e2m1 conversions:
+// round-to-nearest (exact for finite inputs) or stochastic rounding with one
+// 16-bit draw per element; tiles holding a NaN or an infinity use the
+// software encoder.  The scale byte comes from the exact fp32 -> e4m3
+// conversion.
+//
+// Outputs: each lane pair swaps one code word so that the even lane stores
+// 8 bytes of row 2w and the odd lane 8 bytes of row 2w + 1 (each wave store
+// covers 256 contiguous bytes of both rows).  A lane's two rows make one code
+// byte for each of its eight columns (row 2w low nibble, row 2w + 1 high): the
+// byte goes to LDS, into the column's 128-byte segment (16 strips x 8 bytes),
+// and after the last strip 16 lanes per column write whole segments.  The
+// 8-byte words of a column's segment are rotated by the writing lane's index,
+// which spreads the byte writes of a wave over the LDS banks.  The next strip
+// is prefetched into registers while the current one is encoded.
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 #include "nvfp4_plan.hpp"
 
 namespace nvfp4 {
 
-constexpr int k2dTiles = k2dThreads / 16;   // tiles side by side
+constexpr int k2dTiles = k2dThreads / 16;  // tiles side by side (32)
+constexpr int k2dWaves = k2dThreads / 64;  // waves per workgroup; each owns 2 rows of a strip
+#ifndef K2D_PREFETCH
+#define K2D_PREFETCH 1
+#endif
+constexpr int k2dPrefetch = K2D_PREFETCH;  // strips loaded ahead of the one being encoded
 
-// Max over the 16 lanes of a DPP row (every lane of the row gets it): two
-// quad permutations, then the half-row and row mirrors.
-NV_DEV uint32_t row16_max_u32(uint32_t v) {
-  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);
-  v = o > v ? o : v;
-  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);
-  v = o > v ? o : v;
-  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false);
-  v = o > v ? o : v;
-  o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false);
-  return o > v ? o : v;
+// Lane-pair partner's value (DPP quad permutation [1, 0, 3, 2]).
+NV_DEV uint32_t pair_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
 }
 
-constexpr int kColStride = kStrips + 1;  // uint2 per column in the column buffer (+1 spreads banks)
+// Largest magnitude among N values as an fp32 bit pattern with NaNs dropped
+// (0 for none), plus whether a NaN was seen.  Integer order of magnitude bit
+// patterns is value order; patterns above 0x7F800000 are NaNs.
+template <int N>
+NV_DEV void absmax_nan_drop(const float* v, uint32_t& nd, uint32_t& fl) {
+  uint32_t raw = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t m = f2bits(v[i]) & 0x7FFFFFFFu;
+    raw = m > raw ? m : raw;
+  }
+  fl = 0u;
+  nd = raw;
+  if (raw > 0x7F800000u) {
+    fl = 1u;
+    nd = 0u;
+    for (int i = 0; i < N; ++i) {
+      const uint32_t m = f2bits(v[i]) & 0x7FFFFFFFu;
+      if (m <= 0x7F800000u && m > nd) nd = m;
+    }
+  }
+}
+
+// NaN-dropping amax bits (fp32 pattern) and NaN flag of a lane's two rows of
+// eight elements, from the raw loaded words.  bf16: the max of the 16-bit
+// magnitude patterns of each half-word (one packed max per word); a pattern
+// above 0x7F80 flags a NaN, then the slow NaN-dropping scan runs.
+NV_DEV void lane_amax(const uint4* r, const uint16_t*, uint32_t& nd, uint32_t& fl) {
+  const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  us2 m = __builtin_bit_cast(us2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[i] & 0x7FFF7FFFu));
+  uint32_t h = m.x > m.y ? m.x : m.y;
+  fl = 0u;
+  if (h > 0x7F80u) {
+    fl = 1u;
+    h = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t e = (w[i >> 1] >> (16 * (i & 1))) & 0x7FFFu;
+      if (e <= 0x7F80u && e > h) h = e;
+    }
+  }
+  nd = h << 16;
+}
+
+NV_DEV void lane_amax(const uint4* r, const float*, uint32_t& nd, uint32_t& fl) {
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[4 * i] = bits2f(r[i].x);
+    v[4 * i + 1] = bits2f(r[i].y);
+    v[4 * i + 2] = bits2f(r[i].z);
+    v[4 * i + 3] = bits2f(r[i].w);
+  }
+  absmax_nan_drop<16>(v, nd, fl);
+}
+
+// Eight values of one row: load (bf16 or fp32) and widen to fp32.
+template <typename InT>
+struct Row8 {
+  static constexpr int kU4 = sizeof(InT) * 8 / 16;  // uint4 per 8 elements
+};
+
+NV_DEV void widen8(const uint4* r, const uint16_t*, float x[8]) {
+  const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bits2f(w[i] << 16);
+    x[2 * i + 1] = bits2f(w[i] & 0xFFFF0000u);
+  }
+}
+
+NV_DEV void widen8(const uint4* r, const float*, float x[8]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    x[4 * i] = bits2f(r[i].x);
+    x[4 * i + 1] = bits2f(r[i].y);
+    x[4 * i + 2] = bits2f(r[i].z);
+    x[4 * i + 3] = bits2f(r[i].w);
+  }
+}
+
+// Software codes of eight elements (any input; a NaN encodes +6, code 0x7),
+// round-to-nearest or stochastic with draws from the pcg words of their four
+// pairs.
+template <bool SR>
+NV_DEV uint32_t encode8_sw(const float x[8], float rho, uint32_t p0, uint32_t key) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = fabsf(x[i]) * rho;
+    float q;
+    uint32_t mag;
+    if (SR) mag = e2m1_sr(v, (pcg_hash((p0 + (uint32_t)(i >> 1)) ^ key) >> ((i & 1) * 16)) & 0xFFFFu, q);
+    else mag = e2m1_rtn(v, q);
+    const uint32_t neg = (v != v) ? 0u : (f2bits(x[i]) >> 31);
+    c |= (mag | (neg << 3)) << (4 * i);
+  }
+  return c;
+}
+
+// Hardware codes of eight finite-or-infinite elements (pair index p0 of the
+// first two, for the draws).
+template <bool SR>
+NV_DEV uint32_t encode8_hw(const float x[8], float rho, uint32_t p0, uint32_t key) {
+  if (SR) {
+    uint32_t nw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nw[j] = ~pcg_hash((p0 + (uint32_t)j) ^ key);
+    return hw_fp4_sr_word(x, rho, nw);
+  }
+  uint32_t c = any_u32();
+  c = hw_fp4_pair<0>(c, x[0] * rho, x[1] * rho);
+  c = hw_fp4_pair<1>(c, x[2] * rho, x[3] * rho);
+  c = hw_fp4_pair<2>(c, x[4] * rho, x[5] * rho);
+  c = hw_fp4_pair<3>(c, x[6] * rho, x[7] * rho);
+  return c;
+}
 
 template <typename InT, bool SR, bool GLOBAL, bool COL, bool UP>
 __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     const InT* __restrict__ x, const float* __restrict__ global_amax, uint32_t key, int64_t M,
     int64_t K, uint8_t* __restrict__ packed_row, uint8_t* __restrict__ packed_col,
     uint8_t* __restrict__ tile_scales, int64_t ncolg) {
-  __shared__ uint4 stage[k2dTiles * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (bank spread)
-  __shared__ uint2 colbuf[COL ? k2dThreads * kColStride : 1];
-  const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
+  constexpr int kU4 = Row8<InT>::kU4;
+  // tile amax exchange: [strip parity][tile][wave] = (NaN-dropped max bits, NaN seen)
+  __shared__ __align__(16) uint2 red[2][k2dTiles * k2dWaves];
+  // column segments: [column][16 words of 8 bytes], word of strip st at (st + lane) & 15
+  __shared__ uint2 colbuf[COL ? k2dThreads * kStrips : 1];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   // Strip groups are taken from the bottom of the tensor up: the per-tensor
   // amax pass that precedes this one streams the tensor top to bottom, so
   // its most recently read (last-level-cache resident) rows come first here.
   const int64_t nsg = (M / 16 + kStrips - 1) / kStrips;
   const int64_t rsg = (int64_t)blockIdx.x / ncolg, cg = (int64_t)blockIdx.x - rsg * ncolg;
   const int64_t sg = nsg - 1 - rsg;
-  const int64_t col0 = cg * k2dThreads + 16 * t;
-  const bool active = col0 < K;  // uniform over the 16 lanes of a tile
+  const int64_t c0 = cg * k2dThreads + 8 * lane;  // first column of this lane
+  const bool active = c0 < K;                     // uniform over the tile's lane pair
   const int64_t nstrips_total = M / 16;
   const int nst = (int)((nstrips_total - sg * kStrips) < kStrips ? (nstrips_total - sg * kStrips) : kStrips);
+  const int64_t rowA0 = sg * kStrips * 16 + 2 * wv;  // row 2w of the first strip
 
   float S_dec = 1.0f, mul = 0.0f;
   if (GLOBAL) {
@@ -67,139 +197,119 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     global_scales(global_amax[0], 2688.0f, S_enc, S_dec);
     mul = S_enc * (1.0f / 6.0f);
   }
+  // encode reciprocals of all 127 scale codes (ordered before their first
+  // use by the first strip's barrier)
+  __shared__ float rhoT[128];
+  if (threadIdx.x < 127) rhoT[threadIdx.x] = encode_reciprocal(e4m3_decode(threadIdx.x), S_dec);
 
-  // The next strip's 16 elements are loaded while the current one is
-  // encoded (two register buffers of raw input).
-  constexpr int kRaw = sizeof(InT) * 16 / 16;  // uint4 per 16 elements
-  uint4 nxt[kRaw];
-  if (active) {
-    const uint4* p = reinterpret_cast<const uint4*>(x + (sg * kStrips * 16 + r) * K + col0);
+  // Loads are unconditional (no branch, so no merge of old and new register
+  // contents that would make the prefetch wait): a lane past the last column
+  // reads the tensor's last 8 columns, and a load past the last strip reads
+  // the last strip again.  Neither is stored.
+  const int64_t cl = active ? c0 : K - 8;
+  auto load = [&](int st, uint4* d) {
+    const InT* p = x + (rowA0 + 16 * (st < nst ? st : nst - 1)) * K + cl;
 #pragma unroll
-    for (int i = 0; i < kRaw; ++i) nxt[i] = p[i];
-  }
-  for (int st = 0; st < nst; ++st) {
-    const int64_t row0 = (sg * kStrips + st) * 16;
-    const int64_t row = row0 + r;
-    uint4 cur[kRaw];
+    for (int i = 0; i < kU4; ++i) d[i] = reinterpret_cast<const uint4*>(p)[i];
 #pragma unroll
-    for (int i = 0; i < kRaw; ++i) cur[i] = nxt[i];
-    if (active && st + 1 < nst) {
-      const uint4* p = reinterpret_cast<const uint4*>(x + (row + 16) * K + col0);
-#pragma unroll
-      for (int i = 0; i < kRaw; ++i) nxt[i] = p[i];
-    }
-    float xv[16];
-    uint32_t ab = 0;  // magnitude bit patterns: integer max = value max; >= 0x7F800000 flags NaN/inf
-    if (active) {
-      load16(reinterpret_cast<const InT*>(cur), xv);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t m = f2bits(xv[i]) & 0x7FFFFFFFu;
-        ab = m > ab ? m : ab;
-      }
-    }
-    ab = row16_max_u32(ab);
-    const bool special = ab >= 0x7F800000u;
-    float a = bits2f(ab);
-    if (special) {  // NaN-dropping tile amax (all 16 lanes of the tile take this branch)
-      float l = 0.0f;
-      if (active) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) l = fmaxf(l, abs_nan0(xv[i]));
-      }
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) l = fmaxf(l, __shfl_xor(l, off, 64));
-      a = l;
-    }
+    for (int i = 0; i < kU4; ++i) d[kU4 + i] = reinterpret_cast<const uint4*>(p + K)[i];
+  };
 
-    uint32_t c0 = 0, c1 = 0;
-    if (active) {
-      float sigma = GLOBAL ? a * mul : div_guarded(a, 6.0f, 1.0f / 6.0f);
-      sigma = fminf(sigma, kE4m3Max);
-      uint32_t sc = hw_e4m3_pair(sigma, 0.0f) & 0xFFu;
-      float s = e4m3_decode(sc);
-      if (UP && s < sigma && sc < 0x7Eu) {  // truncation-free: smallest e4m3 value >= sigma
-        sc += 1u;
-        s = e4m3_decode(sc);
-      }
-      const float rho = encode_reciprocal(s, S_dec);
-      if (SR && !special) {
-        // stochastic rounding by the hardware conversion, one draw per element
-        const uint32_t p0 = (uint32_t)((row * K + col0) >> 1);
-        uint32_t nw[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) nw[j] = ~pcg_hash((p0 + j) ^ key);
-        c0 = hw_fp4_sr_word(xv, rho, nw);
-        c1 = hw_fp4_sr_word(xv + 8, rho, nw + 4);
-      } else if (!SR && !special) {
-        c0 = hw_fp4_pair<0>(c0, xv[0] * rho, xv[1] * rho);
-        c0 = hw_fp4_pair<1>(c0, xv[2] * rho, xv[3] * rho);
-        c0 = hw_fp4_pair<2>(c0, xv[4] * rho, xv[5] * rho);
-        c0 = hw_fp4_pair<3>(c0, xv[6] * rho, xv[7] * rho);
-        c1 = hw_fp4_pair<0>(c1, xv[8] * rho, xv[9] * rho);
-        c1 = hw_fp4_pair<1>(c1, xv[10] * rho, xv[11] * rho);
-        c1 = hw_fp4_pair<2>(c1, xv[12] * rho, xv[13] * rho);
-        c1 = hw_fp4_pair<3>(c1, xv[14] * rho, xv[15] * rho);
-      } else {
-        uint32_t w[8];
-        if (SR) {
-          const uint32_t p0 = (uint32_t)((row * K + col0) >> 1);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) w[j] = pcg_hash((p0 + j) ^ key);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float v = fabsf(xv[i]) * rho;
-          float q;
-          uint32_t mag;
-          if (SR) mag = e2m1_sr(v, (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu, q);
-          else mag = e2m1_rtn(v, q);
-          const uint32_t neg = (v != v) ? 0u : (f2bits(xv[i]) >> 31);
-          const uint32_t code = mag | (neg << 3);
-          if (i < 8) c0 |= code << (4 * i);
-          else c1 |= code << (4 * (i - 8));
-        }
-      }
-      *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(c0, c1);
-      if (r == 0) tile_scales[(row0 / 16) * (K / 16) + col0 / 16] = (uint8_t)sc;
+  auto process = [&](int st, const uint4* cur) {
+    const int64_t rowA = rowA0 + 16 * st;
+    uint32_t nd = 0, fl = 0;
+    if (active) lane_amax(cur, static_cast<const InT*>(nullptr), nd, fl);
+    // tile amax: lane pair, then the eight waves
+    {
+      const uint32_t o = pair_swap(nd), f = pair_swap(fl);
+      nd = o > nd ? o : nd;
+      fl |= f;
     }
+    uint2* rt = &red[st & 1][(lane >> 1) * k2dWaves];
+    if ((lane & 1) == 0) rt[wv] = make_uint2(nd, fl);
+    __syncthreads();
+    {
+      const uint4* r4 = reinterpret_cast<const uint4*>(rt);
+      nd = 0;
+      fl = 0;
+#pragma unroll
+      for (int i = 0; i < k2dWaves / 2; ++i) {
+        const uint4 v = r4[i];
+        nd = v.x > nd ? v.x : nd;
+        nd = v.z > nd ? v.z : nd;
+        fl |= v.y | v.w;
+      }
+    }
+    if (!active) return;
+    const bool special = fl != 0u || nd == 0x7F800000u;  // a NaN or an infinity in the tile
+    const float a = bits2f(nd);
+    float sigma = GLOBAL ? a * mul : div_guarded(a, 6.0f, 1.0f / 6.0f);
+    sigma = fminf(sigma, kE4m3Max);
+    uint32_t sc = hw_e4m3_pair(sigma, 0.0f) & 0xFFu;
+    if (UP && e4m3_decode(sc) < sigma && sc < 0x7Eu) sc += 1u;  // truncation-free: smallest e4m3 value >= sigma
+    const float rho = rhoT[sc];
+    float xa[8], xb[8];
+    widen8(cur, static_cast<const InT*>(nullptr), xa);
+    widen8(cur + kU4, static_cast<const InT*>(nullptr), xb);
+    const uint32_t pA = (uint32_t)((rowA * K + c0) >> 1), pB = (uint32_t)(((rowA + 1) * K + c0) >> 1);
+    uint32_t ca, cb;
+    if (!special) {
+      ca = encode8_hw<SR>(xa, rho, pA, key);
+      cb = encode8_hw<SR>(xb, rho, pB, key);
+    } else {
+      ca = encode8_sw<SR>(xa, rho, pA, key);
+      cb = encode8_sw<SR>(xb, rho, pB, key);
+    }
+    // rows: the even lane stores row 2w (its word, then its partner's), the
+    // odd lane row 2w + 1 (its partner's word, then its own)
+    const uint32_t oa = pair_swap(ca), ob = pair_swap(cb);
+    if ((lane & 1) == 0)
+      *reinterpret_cast<uint2*>(packed_row + rowA * (K / 2) + c0 / 2) = make_uint2(ca, oa);
+    else
+      *reinterpret_cast<uint2*>(packed_row + (rowA + 1) * (K / 2) + (c0 - 8) / 2) = make_uint2(ob, cb);
+    if (wv == 0 && (lane & 1) == 0)
+      tile_scales[(sg * kStrips + st) * (K / 16) + c0 / 16] = (uint8_t)sc;
     if (COL) {
-      // Stage the 16 codes of this tile row one per byte; lane (t, c) then
-      // gathers column c of its tile (rows 0..15, two codes per byte in row
-      // order) into the column buffer slot of this strip.
-      if (active) {
-        stage[17 * t + r] = make_uint4(
-            (c0 & 0xFu) | ((c0 >> 4) & 0xFu) << 8 | ((c0 >> 8) & 0xFu) << 16 | ((c0 >> 12) & 0xFu) << 24,
-            ((c0 >> 16) & 0xFu) | ((c0 >> 20) & 0xFu) << 8 | ((c0 >> 24) & 0xFu) << 16 | ((c0 >> 28) & 0xFu) << 24,
-            (c1 & 0xFu) | ((c1 >> 4) & 0xFu) << 8 | ((c1 >> 8) & 0xFu) << 16 | ((c1 >> 12) & 0xFu) << 24,
-            ((c1 >> 16) & 0xFu) | ((c1 >> 20) & 0xFu) << 8 | ((c1 >> 24) & 0xFu) << 16 | ((c1 >> 28) & 0xFu) << 24);
-      }
-      __syncthreads();
-      if (active) {
-        const uint8_t* tile = reinterpret_cast<const uint8_t*>(&stage[17 * t]);
-        const int c = r;
-        uint32_t o0 = 0, o1 = 0;
+      // code byte of column j: row 2w in the low nibble, row 2w + 1 in the high
+      const uint32_t ev = (ca & 0x0F0F0F0Fu) | ((cb << 4) & 0xF0F0F0F0u);  // columns 0, 2, 4, 6
+      const uint32_t od = ((ca >> 4) & 0x0F0F0F0Fu) | (cb & 0xF0F0F0F0u);  // columns 1, 3, 5, 7
+      uint8_t* cb8 = reinterpret_cast<uint8_t*>(colbuf) + (8 * lane) * (kStrips * 8) +
+                     ((st + lane) & (kStrips - 1)) * 8 + wv;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const uint32_t code = tile[16 * rr + c];
-          if (rr < 8) o0 |= code << (4 * rr);
-          else o1 |= code << (4 * (rr - 8));
-        }
-        colbuf[(16 * t + c) * kColStride + st] = make_uint2(o0, o1);
+      for (int k = 0; k < 4; ++k) {
+        cb8[(2 * k) * (kStrips * 8)] = (uint8_t)(ev >> (8 * k));
+        cb8[(2 * k + 1) * (kStrips * 8)] = (uint8_t)(od >> (8 * k));
       }
-      __syncthreads();
+    }
+  };
+
+  // A ring of kRing register buffers keeps kPrefetch strips in flight while
+  // one is encoded; the loop is unrolled by the ring size so every buffer
+  // stays in fixed registers (no copies, which would wait for the loads).
+  constexpr int kRing = k2dPrefetch + 1;
+  uint4 raw[kRing][2 * kU4];
+#pragma unroll
+  for (int k = 0; k < k2dPrefetch; ++k) load(k, raw[k]);
+  for (int st0 = 0; st0 < nst; st0 += kRing) {
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) {
+      const int st = st0 + k;
+      if (st < nst) {
+        load(st + k2dPrefetch, raw[(k + k2dPrefetch) % kRing]);
+        process(st, raw[k]);
+      }
     }
   }
   if (COL) {
-    // Each column of this workgroup owns nst * 8 contiguous bytes of its
-    // packed_col row; 16 lanes write one column (8 bytes each), so every
-    // store instruction covers four whole column segments.
+    __syncthreads();
+    // 16 lanes per column, one 8-byte word (strip) each: every store
+    // instruction covers four whole column segments
     const int q = threadIdx.x & 15;
     for (int cc = threadIdx.x >> 4; cc < k2dThreads; cc += k2dThreads / 16) {
       const int64_t col = cg * k2dThreads + cc;
       if (col < K && q < nst)
         *reinterpret_cast<uint2*>(packed_col + col * (M / 2) + sg * (kStrips * 8) + q * 8) =
-            colbuf[cc * kColStride + q];
+            colbuf[cc * kStrips + ((q + (cc >> 3)) & (kStrips - 1))];
     }
   }
 }

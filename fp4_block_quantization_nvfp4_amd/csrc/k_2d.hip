@@ -37,10 +37,8 @@ namespace nvfp4 {
 
 constexpr int k2dTiles = k2dThreads / 16;  // tiles side by side (32)
 constexpr int k2dWaves = k2dThreads / 64;  // waves per workgroup; each owns 2 rows of a strip
-#ifndef K2D_PREFETCH
-#define K2D_PREFETCH 1
-#endif
-constexpr int k2dPrefetch = K2D_PREFETCH;  // strips loaded ahead of the one being encoded
+// strips loaded ahead of the one being encoded (two or three measured slower)
+constexpr int k2dPrefetch = 1;
 
 // Lane-pair partner's value (DPP quad permutation [1, 0, 3, 2]).
 NV_DEV uint32_t pair_swap(uint32_t v) {

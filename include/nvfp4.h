@@ -35,6 +35,20 @@
  *   printed and nothing aborts.  An empty tensor (M == 0 or K == 0) returns
  *   NVFP4_OK and launches nothing, except that nvfp4_amax writes 0.
  *
+ * Signature choices
+ * - `stream` is a hipStream_t passed as void*, so that this header needs no
+ *   HIP include and plain C callers (ctypes, other languages) can use it.
+ * - The second-level scale is chosen by nvfp4_scale_mode (NONE, TENSOR,
+ *   ROW): it selects the amax shape for nvfp4_amax, nvfp4_quantize_4over6
+ *   and nvfp4_dequantize alike.
+ * - Only the per-tensor amax needs device scratch, so its size query is
+ *   nvfp4_amax_workspace_bytes (nvfp4_amax_noalloc needs none).
+ * - nvfp4_quantize_4over6 computes the row amax in the same pass when
+ *   amax_is_input is 0 (the pass holds each row on chip), so it takes a
+ *   writable amax pointer; nvfp4_quantize_2d takes the truncation-free flag
+ *   of its tile scale; nvfp4_dequantize takes the producer's scale mode and
+ *   bound.
+ *
  * Numerics (identical on every path; the CPU oracle is the reference)
  * - x' = x + r when a residual r is given (error feedback), one fp32 add.
  * - Block amax a = NaN-dropping max of |x'| (all-NaN block -> 0).

@@ -117,11 +117,12 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
 
   // Loads are unconditional (no branch, so no merge of old and new register
   // contents that would make the prefetch wait): a lane past the last column
-  // reads the tensor's last 8 columns, and a load past the last strip reads
-  // the last strip again.  Neither is stored.
+  // reads the tensor's last 8 columns, and the load past the last strip reads
+  // the tensor's first two rows' first 8 columns on every lane (a few cache
+  // lines instead of a 16th of the input again).  Neither is stored.
   const int64_t cl = active ? c0 : K - 8;
   auto load = [&](int st, uint4* d) {
-    const InT* p = x + (rowA0 + 16 * (st < nst ? st : nst - 1)) * K + cl;
+    const InT* p = st < nst ? x + (rowA0 + 16 * st) * K + cl : x;
     typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int i = 0; i < kU4; ++i) {

@@ -114,9 +114,9 @@ NV_DEV float absmax_nan_drop16(const float v[16]) {
 }
 
 // Standard 1x16 block with a global scale: sigma = a * mul, mul =
-// S_enc * (1/6); returns the scale byte, codes in c.
-NV_DEV uint32_t block_standard(const float v[16], float mul, float S_dec, uint32_t c[2]) {
-  const uint32_t ab = absmax_bits16(v);
+// S_enc * (1/6); ab is the block's largest magnitude bit pattern (a NaN
+// pattern tops it); returns the scale byte, codes in c.
+NV_DEV uint32_t block_standard(const float v[16], uint32_t ab, float mul, float S_dec, uint32_t c[2]) {
   if (ab < 0x7F800000u) {
     const uint32_t sc = hw_e4m3_pair(fminf(bits2f(ab) * mul, kE4m3Max), 0.0f) & 0xFFu;
     encode16_hw(v, encode_reciprocal(e4m3_decode(sc), S_dec), c);
@@ -138,6 +138,27 @@ struct Raw16 {
     for (int i = 0; i < kWords; ++i) w[i] = q[i];
   }
   NV_DEV void to_f32(float v[16]) const { load16(reinterpret_cast<const InT*>(w), v); }
+  // largest magnitude bit pattern as fp32 bits (bf16: one packed 16-bit max
+  // per word); a NaN pattern tops it
+  NV_DEV uint32_t absmax_bits() const {
+    if constexpr (sizeof(InT) == 2) {
+      typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+      const uint32_t u[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+      us2 m = __builtin_bit_cast(us2, u[0] & 0x7FFF7FFFu);
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, u[i] & 0x7FFF7FFFu));
+      return (uint32_t)(m.x > m.y ? m.x : m.y) << 16;
+    } else {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u[4] = {w[i].x & 0x7FFFFFFFu, w[i].y & 0x7FFFFFFFu, w[i].z & 0x7FFFFFFFu, w[i].w & 0x7FFFFFFFu};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = u[j] > m ? u[j] : m;
+      }
+      return m;
+    }
+  }
 };
 
 // LDS staging of one 16x16 tile of raw input for the columnwise blocks:
@@ -154,6 +175,7 @@ struct StageTile {
 #pragma unroll
     for (int i = 0; i < Raw16<InT>::kWords; ++i) d[i] = raw.w[i];
   }
+
   NV_DEV static void get_col(const uint8_t* tile, int c, float v[16]) {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -187,7 +209,12 @@ __global__ __launch_bounds__(NT) void k_rowcol(
     const InT* __restrict__ x, const float* __restrict__ global_amax, float D, int64_t M, int64_t K,
     uint8_t* __restrict__ packed_row, uint8_t* __restrict__ scales_row,
     uint8_t* __restrict__ packed_col, uint8_t* __restrict__ scales_col, int64_t ncolg) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[(NT / 16) * StageTile<InT>::kTile];
+  // The raw input is staged (fp32 staging of the widened values would spare
+  // the column pass its conversions, but the extra LDS cuts the resident
+  // workgroups of the four-over-six form from 6 to 5 per CU: 121.7 ->
+  // 143.1 us).
+  using ST = StageTile<InT>;
+  __shared__ __attribute__((aligned(16))) uint8_t xs[(NT / 16) * ST::kTile];
   __shared__ uint2 colbuf[NT * (STR + 1)];
   __shared__ uint8_t csbuf[NT * (STR + 1)];
   __shared__ float rhoT[FOS ? 128 : 1];
@@ -233,20 +260,21 @@ __global__ __launch_bounds__(NT) void k_rowcol(
       float v[16];
       cur.to_f32(v);
       uint32_t rc[2];
-      const uint32_t sc = FOS ? fos_block_f32<MSE, true, true>(v, lean, S_enc, S_dec, A, D, rhoT, rc, WT)
-                              : block_standard(v, mul, S_dec, rc);
+      const uint32_t ab = cur.absmax_bits();
+      const uint32_t sc = FOS ? fos_block_ab<MSE, true, true>(v, ab, lean, S_enc, S_dec, A, D, rhoT, rc, WT)
+                              : block_standard(v, ab, mul, S_dec, rc);
       *reinterpret_cast<uint2*>(packed_row + row * (K / 2) + col0 / 2) = make_uint2(rc[0], rc[1]);
       scales_row[row * (K / 16) + col0 / 16] = (uint8_t)sc;
-      StageTile<InT>::put_row(xs + t * StageTile<InT>::kTile, r, cur);
+      ST::put_row(xs + t * ST::kTile, r, cur);
     }
     __syncthreads();
     if (active_c) {
       // lane (tc, c) owns column c of tile tc: rows 0..15 in order
       float v[16];
-      StageTile<InT>::get_col(xs + tc * StageTile<InT>::kTile, c, v);
+      ST::get_col(xs + tc * ST::kTile, c, v);
       uint32_t cc[2];
       const uint32_t sc = FOS ? fos_block_f32<MSE, true, true>(v, lean, S_enc, S_dec, A, D, rhoT, cc, WT)
-                              : block_standard(v, mul, S_dec, cc);
+                              : block_standard(v, absmax_bits16(v), mul, S_dec, cc);
       colbuf[(16 * tc + c) * (STR + 1) + st] = make_uint2(cc[0], cc[1]);
       csbuf[(16 * tc + c) * (STR + 1) + st] = (uint8_t)sc;
     }
@@ -380,16 +408,15 @@ template <typename InT>
 static int launch_rowcol_t(const InT* x, const float* ga, int fos, int mse, float D, int64_t M,
                            int64_t K, uint8_t* pr, uint8_t* sr, uint8_t* pc, uint8_t* sc,
                            hipStream_t st) {
-  constexpr int STR = kRowColStrips;
   int64_t ncolg;
   const LaunchPlan pl = plan_rowcol(M, K, fos);
   const dim3 grid((unsigned)pl.grid), block(pl.block);
   if (!fos) {
-    constexpr int NT = kRowColThreads;
+    constexpr int NT = kRowColThreads, STR = kRowColStrips;
     ncolg = ceil_div(K, NT);
     hipLaunchKernelGGL((k_rowcol<InT, false, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);
   } else {
-    constexpr int NT = kRowColFosThreads;
+    constexpr int NT = kRowColFosThreads, STR = kRowColFosStrips;
     ncolg = ceil_div(K, NT);
     if (mse)
       hipLaunchKernelGGL((k_rowcol<InT, true, true, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, sr, pc, sc, ncolg);

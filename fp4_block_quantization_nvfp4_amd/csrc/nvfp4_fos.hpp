@@ -357,15 +357,13 @@ NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S
 // fos_row_in_range(A, S_dec): the largest magnitude bit pattern tells finite
 // blocks from blocks with a NaN or an infinity (those take fos_block with the
 // NaN-dropping amax); a finite block is plain when 2^-117 <= a <= A.
+// The same with the block's largest magnitude bit pattern ab given (integer
+// max of the |x| patterns: a NaN pattern tops it, so ab >= 0x7F800000 flags a
+// NaN or an infinity).
 template <bool MSE, bool TIES, bool WTAB = false>
-NV_DEV uint32_t fos_block_f32(const float xv[16], bool lean, float S_enc, float S_dec, float A,
-                              float D, const float* rhoT, uint32_t c[2], const float* WT = nullptr) {
-  uint32_t ab = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t m = f2bits(xv[i]) & 0x7FFFFFFFu;
-    ab = m > ab ? m : ab;
-  }
+NV_DEV uint32_t fos_block_ab(const float xv[16], uint32_t ab, bool lean, float S_enc, float S_dec,
+                             float A, float D, const float* rhoT, uint32_t c[2],
+                             const float* WT = nullptr) {
   if (ab < 0x7F800000u) {
     const float a = bits2f(ab);
     return fos_block_plain<MSE, TIES, WTAB>(xv, a, lean && a >= 0x1p-117f && a <= A, S_enc, S_dec, A,
@@ -375,6 +373,18 @@ NV_DEV uint32_t fos_block_f32(const float xv[16], bool lean, float S_enc, float 
 #pragma unroll
   for (int i = 0; i < 16; ++i) a = fmaxf(a, abs_nan0(xv[i]));
   return fos_block<MSE>(xv, a, S_enc, S_dec, A, D, rhoT, c);
+}
+
+template <bool MSE, bool TIES, bool WTAB = false>
+NV_DEV uint32_t fos_block_f32(const float xv[16], bool lean, float S_enc, float S_dec, float A,
+                              float D, const float* rhoT, uint32_t c[2], const float* WT = nullptr) {
+  uint32_t ab = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t m = f2bits(xv[i]) & 0x7FFFFFFFu;
+    ab = m > ab ? m : ab;
+  }
+  return fos_block_ab<MSE, TIES, WTAB>(xv, ab, lean, S_enc, S_dec, A, D, rhoT, c, WT);
 }
 
 }  // namespace nvfp4

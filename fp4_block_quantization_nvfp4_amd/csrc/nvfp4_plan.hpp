@@ -19,7 +19,7 @@ constexpr int k46MaxThreads = 1024;     // k_4over6 (generic): one workgroup per
 constexpr int64_t k46MaxGrid = int64_t(1) << 20;
 constexpr int k2dThreads = 512;         // k_quant2d: columns covered by a workgroup
 constexpr int kStrips = 16;
-constexpr int kRowColThreads = 256, kRowColFosThreads = 128, kRowColStrips = 16;
+constexpr int kRowColThreads = 256, kRowColFosThreads = 128, kRowColStrips = 16, kRowColFosStrips = 16;
 constexpr int k46TileThreads = 512, k46TileStrips = 16;
 constexpr int kAmaxThreads = 256;
 constexpr int kAmaxMaxGroups = 2048;
@@ -78,9 +78,10 @@ inline LaunchPlan plan_quant2d(int64_t M, int64_t K) {
 }
 
 inline int rowcol_threads(int four_over_six) { return four_over_six ? kRowColFosThreads : kRowColThreads; }
+inline int rowcol_strips(int four_over_six) { return four_over_six ? kRowColFosStrips : kRowColStrips; }
 inline LaunchPlan plan_rowcol(int64_t M, int64_t K, int four_over_six) {
   const int nt = rowcol_threads(four_over_six);
-  return {PLAN_ROWCOL, 1, xcd_grid(ceil_div(K, nt) * ceil_div(M / 16, kRowColStrips)), nt};
+  return {PLAN_ROWCOL, 1, xcd_grid(ceil_div(K, nt) * ceil_div(M / 16, rowcol_strips(four_over_six))), nt};
 }
 
 inline LaunchPlan plan_4over6_2d(int64_t M, int64_t K) {

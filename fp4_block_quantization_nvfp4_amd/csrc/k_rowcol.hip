@@ -289,7 +289,6 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
     uint8_t* __restrict__ packed_row, uint8_t* __restrict__ packed_col,
     uint8_t* __restrict__ tile_scales, int64_t ncolg) {
   __shared__ float rhoT[128];
-  __shared__ uint4 stage[(NT / 16) * 17];  // per tile 16 rows of 16 code bytes, tile stride 17 (banks)
   __shared__ uint2 colbuf[COL ? NT * (STR + 1) : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
   const int64_t nwork = ncolg * ((M / 16 + STR - 1) / STR);
@@ -320,7 +319,7 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
     uint32_t ab = 0;
     if (active) {
       cur.to_f32(v);
-      ab = absmax_bits16(v);
+      ab = cur.absmax_bits();
     }
     ab = row16_max(ab);
     // NaN-dropping tile amax (the integer max of the magnitude bits is the
@@ -378,29 +377,32 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
       if (r == 0) tile_scales[(row0 / 16) * (K / 16) + col0 / 16] = (uint8_t)(pick4 ? k4 : k6);
     }
     if (COL) {
+      // Column codes: rows 2k and 2k + 1 of the tile (lanes r = 2k, 2k + 1,
+      // a DPP quad pair) make byte k of each column's strip word; the even
+      // lane writes the bytes of columns 0..7, the odd lane those of 8..15.
+      // The column buffer is written out once after the last strip, so no
+      // barrier is needed here.
+      const uint32_t p0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)c0, 0xB1, 0xF, 0xF, false);
+      const uint32_t p1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)c1, 0xB1, 0xF, 0xF, false);
       if (active) {
-        stage[17 * t + r] = make_uint4(
-            (c0 & 0xFu) | ((c0 >> 4) & 0xFu) << 8 | ((c0 >> 8) & 0xFu) << 16 | ((c0 >> 12) & 0xFu) << 24,
-            ((c0 >> 16) & 0xFu) | ((c0 >> 20) & 0xFu) << 8 | ((c0 >> 24) & 0xFu) << 16 | ((c0 >> 28) & 0xFu) << 24,
-            (c1 & 0xFu) | ((c1 >> 4) & 0xFu) << 8 | ((c1 >> 8) & 0xFu) << 16 | ((c1 >> 12) & 0xFu) << 24,
-            ((c1 >> 16) & 0xFu) | ((c1 >> 20) & 0xFu) << 8 | ((c1 >> 24) & 0xFu) << 16 | ((c1 >> 28) & 0xFu) << 24);
-      }
-      __syncthreads();
-      if (active) {
-        const uint8_t* tile = reinterpret_cast<const uint8_t*>(&stage[17 * t]);
-        uint32_t o0 = 0, o1 = 0;
+        const bool odd = r & 1;
+        const uint32_t lo = odd ? p1 : c0;  // row 2k, this lane's eight columns
+        const uint32_t hi = odd ? c1 : p0;  // row 2k + 1
+        const uint32_t ev = (lo & 0x0F0F0F0Fu) | ((hi << 4) & 0xF0F0F0F0u);  // columns 0, 2, 4, 6
+        const uint32_t od = ((lo >> 4) & 0x0F0F0F0Fu) | (hi & 0xF0F0F0F0u);  // columns 1, 3, 5, 7
+        uint8_t* cb = reinterpret_cast<uint8_t*>(colbuf) + ((16 * t + (odd ? 8 : 0)) * (STR + 1) + st) * 8 + (r >> 1);
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const uint32_t code = tile[16 * rr + r];
-          if (rr < 8) o0 |= code << (4 * rr);
-          else o1 |= code << (4 * (rr - 8));
+        for (int k = 0; k < 4; ++k) {
+          cb[(2 * k) * (STR + 1) * 8] = (uint8_t)(ev >> (8 * k));
+          cb[(2 * k + 1) * (STR + 1) * 8] = (uint8_t)(od >> (8 * k));
         }
-        colbuf[(16 * t + r) * (STR + 1) + st] = make_uint2(o0, o1);
       }
-      __syncthreads();
     }
   }
-  if (COL) flush_columns<NT, STR>(colbuf, nullptr, cg, sg, nst, M, K, packed_col, nullptr);
+  if (COL) {
+    __syncthreads();
+    flush_columns<NT, STR>(colbuf, nullptr, cg, sg, nst, M, K, packed_col, nullptr);
+  }
 }
 
 

@@ -114,11 +114,13 @@ __global__ __launch_bounds__(kThreads) void k_quant1x16(
   uint32_t codes;
   float xh[4];
   if (SR && !special) {
-    // stochastic rounding by the hardware conversion, one draw per element
-    const uint32_t p0 = (uint32_t)(g * 2);
-    const uint32_t t0 = hw_fp4_sr_pair<0>(xv[0] * rho, xv[1] * rho, ~pcg_hash(p0 ^ key));
-    const uint32_t t1 = hw_fp4_sr_pair<1>(xv[2] * rho, xv[3] * rho, ~pcg_hash((p0 + 1u) ^ key));
-    codes = (t0 & 0xFFu) | (t1 & 0xFF00u);
+    // stochastic rounding by the hardware conversion, one draw per element;
+    // the lane's first pair index 2g is even
+    uint32_t w[2];
+    pcg_group(pcg_group_key<2>(key), (uint32_t)(g * 2), w);
+    const uint32_t t0 = hw_fp4_sr_pair<0>(xv[0] * rho, xv[1] * rho, ~w[0]);
+    const uint32_t t1 = hw_fp4_sr_pair<1>(xv[2] * rho, xv[3] * rho, ~w[1]);
+    codes = __builtin_amdgcn_perm(t1, t0, 0x0C0C0500u);  // byte 0 of t0, byte 1 of t1
     if (OUT != 0 || HAS_RES) {
       const nv_f2 q01 = hw_fp4_values<0>(codes);
       const nv_f2 q23 = hw_fp4_values<1>(codes);
@@ -139,19 +141,15 @@ __global__ __launch_bounds__(kThreads) void k_quant1x16(
       xh[3] = (q23.y * s) * S_dec;
     }
   } else {
-    uint32_t w0 = 0, w1 = 0;
-    if (SR) {
-      const uint32_t p0 = (uint32_t)(g * 2);
-      w0 = pcg_hash(p0 ^ key);
-      w1 = pcg_hash((p0 + 1u) ^ key);
-    }
+    uint32_t w[2] = {0u, 0u};
+    if (SR) pcg_group(pcg_group_key<2>(key), (uint32_t)(g * 2), w);
     codes = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float v = fabsf(xv[i]) * rho;
       float q;
       uint32_t mag;
-      if (SR) mag = e2m1_sr(v, ((i < 2 ? w0 : w1) >> ((i & 1) * 16)) & 0xFFFFu, q);
+      if (SR) mag = e2m1_sr(v, (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu, q);
       else mag = e2m1_rtn(v, q);
       const bool nan_v = (v != v);
       const uint32_t neg = nan_v ? 0u : (f2bits(xv[i]) >> 31);

@@ -46,16 +46,18 @@ constexpr int k2dPrefetch = 1;
 
 // Software codes of eight elements (any input; a NaN encodes +6, code 0x7),
 // round-to-nearest or stochastic with draws from the pcg words of their four
-// pairs.
+// pairs (p0 a multiple of four).
 template <bool SR>
-NV_DEV uint32_t encode8_sw(const float x[8], float rho, uint32_t p0, uint32_t key) {
+NV_DEV uint32_t encode8_sw(const float x[8], float rho, uint32_t p0, const PcgGroup<4>& pq) {
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (SR) pcg_group(pq, p0, w);
   uint32_t c = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float v = fabsf(x[i]) * rho;
     float q;
     uint32_t mag;
-    if (SR) mag = e2m1_sr(v, (pcg_hash((p0 + (uint32_t)(i >> 1)) ^ key) >> ((i & 1) * 16)) & 0xFFFFu, q);
+    if (SR) mag = e2m1_sr(v, (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu, q);
     else mag = e2m1_rtn(v, q);
     const uint32_t neg = (v != v) ? 0u : (f2bits(x[i]) >> 31);
     c |= (mag | (neg << 3)) << (4 * i);
@@ -64,13 +66,14 @@ NV_DEV uint32_t encode8_sw(const float x[8], float rho, uint32_t p0, uint32_t ke
 }
 
 // Hardware codes of eight finite-or-infinite elements (pair index p0 of the
-// first two, for the draws).
+// first two, a multiple of four, for the draws).
 template <bool SR>
-NV_DEV uint32_t encode8_hw(const float x[8], float rho, uint32_t p0, uint32_t key) {
+NV_DEV uint32_t encode8_hw(const float x[8], float rho, uint32_t p0, const PcgGroup<4>& pq) {
   if (SR) {
     uint32_t nw[4];
+    pcg_group(pq, p0, nw);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) nw[j] = ~pcg_hash((p0 + (uint32_t)j) ^ key);
+    for (int j = 0; j < 4; ++j) nw[j] = ~nw[j];
     return hw_fp4_sr_word(x, rho, nw);
   }
   uint32_t c = any_u32();
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
   const int nst = (int)((nstrips_total - sg * kStrips) < kStrips ? (nstrips_total - sg * kStrips) : kStrips);
   const int64_t rowA0 = sg * kStrips * 16 + 2 * wv;  // row 2w of the first strip
 
+  const PcgGroup<4> pq = pcg_group_key<4>(key);  // draw words, uniform over the grid
   float S_dec = 1.0f, mul = 0.0f;
   if (GLOBAL) {
     float S_enc;
@@ -120,9 +124,13 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
   // reads the tensor's last 8 columns, and the load past the last strip reads
   // the tensor's first two rows' first 8 columns on every lane (a few cache
   // lines instead of a 16th of the input again).  Neither is stored.
+  // Strips are loaded and encoded in order, so their addresses and pair
+  // indices advance by a fixed step (no per-strip 64-bit multiplies).
   const int64_t cl = active ? c0 : K - 8;
+  const InT* lp = x + rowA0 * K + cl;  // loads of the next strip to load
   auto load = [&](int st, uint4* d) {
-    const InT* p = st < nst ? x + (rowA0 + 16 * st) * K + cl : x;
+    const InT* p = st < nst ? lp : x;
+    lp += 16 * K;
     typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int i = 0; i < kU4; ++i) {
@@ -133,8 +141,15 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     }
   };
 
+  // rowwise store and pair index of row A (a multiple of four, since K and c0
+  // are multiples of eight) of the next strip to encode
+  uint8_t* sp = packed_row + row_dst_offset(rowA0, K, c0, lane);
+  uint32_t pA = (uint32_t)((rowA0 * K + c0) >> 1);
   auto process = [&](int st, const uint4* cur) {
-    const int64_t rowA = rowA0 + 16 * st;
+    uint8_t* const dst = sp;
+    const uint32_t pa = pA, pb = pA + (uint32_t)(K >> 1);
+    sp += 8 * K;
+    pA += (uint32_t)(8 * K);
     uint32_t nd = 0, fl = 0;
     if (active) lane_amax(cur, static_cast<const InT*>(nullptr), nd, fl);
     // tile amax: lane pair, then the eight waves
@@ -169,16 +184,15 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     float xa[8], xb[8];
     widen8(cur, static_cast<const InT*>(nullptr), xa);
     widen8(cur + kU4, static_cast<const InT*>(nullptr), xb);
-    const uint32_t pA = (uint32_t)((rowA * K + c0) >> 1), pB = (uint32_t)(((rowA + 1) * K + c0) >> 1);
     uint32_t ca, cb;
     if (!special) {
-      ca = encode8_hw<SR>(xa, rho, pA, key);
-      cb = encode8_hw<SR>(xb, rho, pB, key);
+      ca = encode8_hw<SR>(xa, rho, pa, pq);
+      cb = encode8_hw<SR>(xb, rho, pb, pq);
     } else {
-      ca = encode8_sw<SR>(xa, rho, pA, key);
-      cb = encode8_sw<SR>(xb, rho, pB, key);
+      ca = encode8_sw<SR>(xa, rho, pa, pq);
+      cb = encode8_sw<SR>(xb, rho, pb, pq);
     }
-    store_rows_pair(packed_row, rowA, K, c0, lane, ca, cb);
+    store_rows_pair(dst, lane, ca, cb);
     if (wv == 0 && (lane & 1) == 0)
       tile_scales[(sg * kStrips + st) * (K / 16) + c0 / 16] = (uint8_t)sc;
     if (COL) stage_col_bytes(colbuf, lane, wv, st, ca, cb);

@@ -101,10 +101,42 @@ NV_DEV uint32_t f32_to_bf16(float f) {
 // ------------------------------------------------------------------- RNG
 // Jarzynski & Olano, "Hash Functions for GPU Rendering" (JCGT 2020), the
 // "pcg" hash: one PCG32 LCG step, then the RXS-M-XS output permutation.
-__host__ __device__ inline uint32_t pcg_hash(uint32_t v) {
-  uint32_t state = v * 747796405u + 2891336453u;
-  uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+constexpr uint32_t kPcgMul = 747796405u, kPcgInc = 2891336453u;
+
+// The output permutation applied to an LCG state.
+__host__ __device__ inline uint32_t pcg_permute(uint32_t state) {
+  const uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
   return (word >> 22u) ^ word;
+}
+
+__host__ __device__ inline uint32_t pcg_hash(uint32_t v) { return pcg_permute(v * kPcgMul + kPcgInc); }
+
+// Draw words pcg_hash((p0 + j) ^ key), j = 0 .. N - 1, of N consecutive
+// pairs (N = 2 or 4) whose first index p0 is a multiple of N.  The low bits
+// of p0 ^ (key & ~(N - 1)) are then clear, so (p0 + j) ^ key equals
+// (p0 ^ (key & ~(N - 1))) + ((key & (N - 1)) ^ j), and by the distributive
+// law mod 2^32 the LCG step is one multiply shared by the N pairs plus a
+// per-pair constant of the key.
+template <int N>
+struct PcgGroup {
+  uint32_t hi;      // key & ~(N - 1)
+  uint32_t inc[N];  // ((key & (N - 1)) ^ j) * kPcgMul + kPcgInc
+};
+
+template <int N>
+__host__ __device__ inline PcgGroup<N> pcg_group_key(uint32_t key) {
+  static_assert(N == 2 || N == 4, "groups of 2 or 4 pairs");
+  PcgGroup<N> q;
+  q.hi = key & ~(uint32_t)(N - 1);
+  for (uint32_t j = 0; j < (uint32_t)N; ++j) q.inc[j] = ((key & (uint32_t)(N - 1)) ^ j) * kPcgMul + kPcgInc;
+  return q;
+}
+
+template <int N>
+NV_DEV void pcg_group(const PcgGroup<N>& q, uint32_t p0, uint32_t w[N]) {
+  const uint32_t base = (p0 ^ q.hi) * kPcgMul;
+#pragma unroll
+  for (int j = 0; j < N; ++j) w[j] = pcg_permute(base + q.inc[j]);
 }
 
 // Per-call key of the (seed, step) stream.
@@ -264,7 +296,11 @@ NV_DEV uint32_t hw_fp4_sr_word(const float* x, float rho, const uint32_t* nw) {
   const uint32_t t1 = hw_fp4_sr_pair<1>(x[2] * rho, x[3] * rho, nw[1]);
   const uint32_t t2 = hw_fp4_sr_pair<2>(x[4] * rho, x[5] * rho, nw[2]);
   const uint32_t t3 = hw_fp4_sr_pair<3>(x[6] * rho, x[7] * rho, nw[3]);
-  return (t0 & 0xFFu) | (t1 & 0xFF00u) | (t2 & 0xFF0000u) | (t3 & 0xFF000000u);
+  // byte j of t_j holds pair j; byte permutes gather them (selector byte
+  // 0-3: that byte of the second operand, 4-7: of the first, 0x0C: zero)
+  const uint32_t lo = __builtin_amdgcn_perm(t1, t0, 0x0C0C0500u);  // t0 byte 0, t1 byte 1
+  const uint32_t hi = __builtin_amdgcn_perm(t3, t2, 0x07020C0Cu);  // t2 byte 2, t3 byte 3
+  return lo | hi;
 }
 
 // gfx950 fp32 -> e4m3 of two scales in [0, 448] (bytes 0 and 1): equal to

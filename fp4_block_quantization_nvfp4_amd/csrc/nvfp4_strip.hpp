@@ -106,14 +106,16 @@ NV_DEV void widen8(const uint4* r, const float*, float x[8]) {
 // row A (= 2w), cb those of row B; the even lane stores 8 bytes of row A (its
 // word, then its partner's), the odd lane 8 bytes of row B (its partner's
 // word, then its own), so a wave store covers 256 contiguous bytes of both
-// rows.  Both lanes of the pair must execute it.
-NV_DEV void store_rows_pair(uint8_t* packed_row, int64_t rowA, int64_t K, int64_t c0, int lane,
-                            uint32_t ca, uint32_t cb) {
+// rows.  Both lanes of the pair must execute it; dst is the lane's 8-byte
+// destination (row_dst_offset).
+NV_DEV void store_rows_pair(uint8_t* dst, int lane, uint32_t ca, uint32_t cb) {
   const uint32_t oa = pair_swap(ca), ob = pair_swap(cb);
-  if ((lane & 1) == 0)
-    *reinterpret_cast<uint2*>(packed_row + rowA * (K / 2) + c0 / 2) = make_uint2(ca, oa);
-  else
-    *reinterpret_cast<uint2*>(packed_row + (rowA + 1) * (K / 2) + (c0 - 8) / 2) = make_uint2(ob, cb);
+  *reinterpret_cast<uint2*>(dst) = (lane & 1) == 0 ? make_uint2(ca, oa) : make_uint2(ob, cb);
+}
+
+// Byte offset of a lane's rowwise store for the strip whose row A is rowA.
+NV_DEV int64_t row_dst_offset(int64_t rowA, int64_t K, int64_t c0, int lane) {
+  return (lane & 1) == 0 ? rowA * (K / 2) + c0 / 2 : (rowA + 1) * (K / 2) + (c0 - 8) / 2;
 }
 
 // Columnwise codes: a lane's two rows give one code byte for each of its

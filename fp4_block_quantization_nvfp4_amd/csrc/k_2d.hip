@@ -13,8 +13,9 @@
 // than 16 rows x 128 bytes.  Tile t of the strip (columns 16t .. 16t + 15) is
 // the lane pair (2t, 2t + 1) of all eight waves: the tile amax is the max over
 // the pair (one DPP swap), then over the eight waves through a small LDS
-// table (one barrier per strip; the table is double-buffered by strip
-// parity).  Codes come from the hardware fp32 -> e2m1 conversions:
+// table.  Strips are taken in groups of two with one barrier per group (one
+// per strip: 7168x18432 SR 81.6 against 83.2 us); the table is
+// double-buffered by group parity.  Codes come from the hardware fp32 -> e2m1 conversions:
 // round-to-nearest (exact for finite inputs) or stochastic rounding with one
 // 16-bit draw per element; tiles holding a NaN or an infinity use the
 // software encoder.  The scale byte comes from the exact fp32 -> e4m3
@@ -27,9 +28,9 @@
 // byte goes to LDS, into the column's 128-byte segment (16 strips x 8 bytes),
 // and after the last strip 16 lanes per column write whole segments.  The
 // 8-byte words of a column's segment are rotated by the writing lane's index,
-// which spreads the byte writes of a wave over the LDS banks.  The next strip
-// is prefetched into registers while the current one is encoded, with
-// nontemporal loads (the input is read once; round-to-nearest 84.8 -> 71.5
+// which spreads the byte writes of a wave over the LDS banks.  The next group
+// of strips is prefetched into registers while the current one is encoded,
+// with nontemporal loads (the input is read once; round-to-nearest 84.8 -> 71.5
 // us at 7168x18432 bf16 against plain loads).
 #include "nvfp4_device.hpp"
 #include "nvfp4_launch.hpp"
@@ -41,8 +42,9 @@ namespace nvfp4 {
 constexpr int k2dTiles = kStripTiles;
 constexpr int k2dWaves = kStripWaves;
 static_assert(k2dThreads == kStripLanes && kStrips == kStripCount, "strip geometry");
-// strips loaded ahead of the one being encoded (two or three measured slower)
-constexpr int k2dPrefetch = 1;
+// strips whose tile amaxes are exchanged under one workgroup barrier; the
+// next group is loaded while one is encoded
+constexpr int k2dGroup = 2;
 
 // Software codes of eight elements (any input; a NaN encodes +6, code 0x7),
 // round-to-nearest or stochastic with draws from the pcg words of their four
@@ -90,8 +92,9 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     int64_t K, uint8_t* __restrict__ packed_row, uint8_t* __restrict__ packed_col,
     uint8_t* __restrict__ tile_scales, int64_t ncolg) {
   constexpr int kU4 = Row8<InT>::kU4;
-  // tile amax exchange: [strip parity][tile][wave] = (NaN-dropped max bits, NaN seen)
-  __shared__ __align__(16) uint2 red[2][k2dTiles * k2dWaves];
+  // tile amax exchange: [group parity][strip of the group][tile][wave] =
+  // (NaN-dropped max bits, NaN seen)
+  __shared__ __align__(16) uint2 red[2][k2dGroup][k2dTiles * k2dWaves];
   // column segments: [column][16 words of 8 bytes], word of strip st at (st + lane) & 15
   __shared__ uint2 colbuf[COL ? k2dThreads * kStrips : 1];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -145,26 +148,24 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
   // are multiples of eight) of the next strip to encode
   uint8_t* sp = packed_row + row_dst_offset(rowA0, K, c0, lane);
   uint32_t pA = (uint32_t)((rowA0 * K + c0) >> 1);
-  auto process = [&](int st, const uint4* cur) {
+  // tile amax of one strip: lane pair, then (after the barrier) the eight
+  // waves; rt is the strip's slot for the lane's tile
+  auto amax_phase = [&](const uint4* cur, uint2* rt) {
+    uint32_t nd = 0, fl = 0;
+    if (active) lane_amax(cur, static_cast<const InT*>(nullptr), nd, fl);
+    const uint32_t o = pair_swap(nd), f = pair_swap(fl);
+    nd = o > nd ? o : nd;
+    fl |= f;
+    if ((lane & 1) == 0) rt[wv] = make_uint2(nd, fl);
+  };
+  auto encode_phase = [&](int st, const uint4* cur, const uint2* rt) {
     uint8_t* const dst = sp;
     const uint32_t pa = pA, pb = pA + (uint32_t)(K >> 1);
     sp += 8 * K;
     pA += (uint32_t)(8 * K);
     uint32_t nd = 0, fl = 0;
-    if (active) lane_amax(cur, static_cast<const InT*>(nullptr), nd, fl);
-    // tile amax: lane pair, then the eight waves
-    {
-      const uint32_t o = pair_swap(nd), f = pair_swap(fl);
-      nd = o > nd ? o : nd;
-      fl |= f;
-    }
-    uint2* rt = &red[st & 1][(lane >> 1) * k2dWaves];
-    if ((lane & 1) == 0) rt[wv] = make_uint2(nd, fl);
-    __syncthreads();
     {
       const uint4* r4 = reinterpret_cast<const uint4*>(rt);
-      nd = 0;
-      fl = 0;
 #pragma unroll
       for (int i = 0; i < k2dWaves / 2; ++i) {
         const uint4 v = r4[i];
@@ -198,20 +199,29 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     if (COL) stage_col_bytes(colbuf, lane, wv, st, ca, cb);
   };
 
-  // A ring of kRing register buffers keeps kPrefetch strips in flight while
-  // one is encoded; the loop is unrolled by the ring size so every buffer
-  // stays in fixed registers (no copies, which would wait for the loads).
-  constexpr int kRing = k2dPrefetch + 1;
+  // Two groups of register buffers: the next group of strips is loaded while
+  // one is reduced and encoded.  The loop is unrolled by the two groups so
+  // every buffer stays in fixed registers (no copies, which would wait for
+  // the loads).  Group parity h alternates the tile amax slots, so a wave
+  // that runs ahead never overwrites slots another wave still reads.
+  constexpr int kRing = 2 * k2dGroup;
   uint4 raw[kRing][2 * kU4];
 #pragma unroll
-  for (int k = 0; k < k2dPrefetch; ++k) load(k, raw[k]);
+  for (int k = 0; k < k2dGroup; ++k) load(k, raw[k]);
+  const int tslot = (lane >> 1) * k2dWaves;
   for (int st0 = 0; st0 < nst; st0 += kRing) {
 #pragma unroll
-    for (int k = 0; k < kRing; ++k) {
-      const int st = st0 + k;
-      if (st < nst) {
-        load(st + k2dPrefetch, raw[(k + k2dPrefetch) % kRing]);
-        process(st, raw[k]);
+    for (int h = 0; h < 2; ++h) {
+      const int g0 = st0 + h * k2dGroup;  // first strip of the group
+      if (g0 < nst) {
+#pragma unroll
+        for (int k = 0; k < k2dGroup; ++k) load(g0 + k2dGroup + k, raw[(1 - h) * k2dGroup + k]);
+#pragma unroll
+        for (int k = 0; k < k2dGroup; ++k) amax_phase(raw[h * k2dGroup + k], &red[h][k][tslot]);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < k2dGroup; ++k)
+          if (g0 + k < nst) encode_phase(g0 + k, raw[h * k2dGroup + k], &red[h][k][tslot]);
       }
     }
   }

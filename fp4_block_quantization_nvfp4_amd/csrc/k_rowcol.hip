@@ -204,7 +204,7 @@ NV_DEV void flush_columns(const uint2* colbuf, const uint8_t* csbuf, int64_t cg,
   }
 }
 
-template <typename InT, bool FOS, bool MSE, int NT, int STR>
+template <typename InT, bool FOS, bool MSE, int NT, int STR, bool RING = !FOS>
 __global__ __launch_bounds__(NT) void k_rowcol(
     const InT* __restrict__ x, const float* __restrict__ global_amax, float D, int64_t M, int64_t K,
     uint8_t* __restrict__ packed_row, uint8_t* __restrict__ scales_row,
@@ -250,12 +250,18 @@ __global__ __launch_bounds__(NT) void k_rowcol(
     __syncthreads();
   }
 
-  Raw16<InT> nxt;
-  if (active) nxt.load(x + (sg * STR * 16 + r) * K + col0);
-  for (int st = 0; st < nst; ++st) {
+  // Loads are unconditional (a lane past the last column reads the row's last
+  // 16 elements, the load past the last strip reads the tensor's first 16),
+  // and a ring of two register buffers, with the loop unrolled by two, keeps
+  // them in fixed registers: no merge of old and new contents, which would
+  // make the next strip's prefetch wait before the current one is encoded.
+  const InT* lp = x + (sg * STR * 16 + r) * K + (active ? col0 : K - 16);
+  auto load = [&](int st, Raw16<InT>& d) {
+    d.load(st < nst ? lp : x);
+    lp += 16 * K;
+  };
+  auto body = [&](int st, const Raw16<InT>& cur) {
     const int64_t row = (sg * STR + st) * 16 + r;
-    const Raw16<InT> cur = nxt;
-    if (active && st + 1 < nst) nxt.load(x + (row + 16) * K + col0);
     if (active) {
       float v[16];
       cur.to_f32(v);
@@ -279,6 +285,27 @@ __global__ __launch_bounds__(NT) void k_rowcol(
       csbuf[(16 * tc + c) * (STR + 1) + st] = (uint8_t)sc;
     }
     __syncthreads();
+  };
+  if constexpr (RING) {
+    Raw16<InT> ring[2];
+    load(0, ring[0]);
+    for (int st0 = 0; st0 < nst; st0 += 2) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (st0 + k < nst) {
+          load(st0 + k + 1, ring[k ^ 1]);
+          body(st0 + k, ring[k]);
+        }
+      }
+    }
+  } else {
+    Raw16<InT> nxt;
+    load(0, nxt);
+    for (int st = 0; st < nst; ++st) {
+      const Raw16<InT> cur = nxt;
+      load(st + 1, nxt);
+      body(st, cur);
+    }
   }
   flush_columns<NT, STR>(colbuf, csbuf, cg, sg, nst, M, K, packed_col, scales_col);
 }
@@ -308,13 +335,15 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
   if (threadIdx.x < 127) rhoT[threadIdx.x] = encode_reciprocal(e4m3_decode(threadIdx.x), S_dec);
   __syncthreads();
 
-  Raw16<InT> nxt;
-  if (active) nxt.load(x + (sg * STR * 16 + r) * K + col0);
-  for (int st = 0; st < nst; ++st) {
+  // unconditional loads (as in k_rowcol); the body is too large to unroll
+  const InT* lp = x + (sg * STR * 16 + r) * K + (active ? col0 : K - 16);
+  auto load = [&](int st, Raw16<InT>& d) {
+    d.load(st < nst ? lp : x);
+    lp += 16 * K;
+  };
+  auto body = [&](int st, const Raw16<InT>& cur) {
     const int64_t row0 = (sg * STR + st) * 16;
     const int64_t row = row0 + r;
-    const Raw16<InT> cur = nxt;
-    if (active && st + 1 < nst) nxt.load(x + (row + 16) * K + col0);
     float v[16];
     uint32_t ab = 0;
     if (active) {
@@ -398,6 +427,13 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
         }
       }
     }
+  };
+  Raw16<InT> nxt;
+  load(0, nxt);
+  for (int st = 0; st < nst; ++st) {
+    const Raw16<InT> cur = nxt;
+    load(st + 1, nxt);
+    body(st, cur);
   }
   if (COL) {
     __syncthreads();

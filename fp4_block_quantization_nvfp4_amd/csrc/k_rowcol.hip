@@ -72,6 +72,17 @@ NV_DEV uint32_t row16_max(uint32_t v) {
   return o > v ? o : v;
 }
 
+// Value of lane i ^ 8, i ^ 4 (given a value already symmetric under ^ 8),
+// i ^ 2 and i ^ 1 within a 16-lane DPP row: a rotation of the row by 8 is
+// the ^ 8 exchange; after it a rotation by 4 delivers the partner i ^ 4's
+// value (lanes i + 4 and i - 4 then hold equal values); the quad
+// permutations [2,3,0,1] and [1,0,3,2] are ^ 2 and ^ 1.  Every lane of the
+// row must be active.
+NV_DEV uint32_t dpp_x8(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false); }
+NV_DEV uint32_t dpp_x4s(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false); }
+NV_DEV uint32_t dpp_x2(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false); }
+NV_DEV uint32_t dpp_x1(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false); }
+
 // Sum of the 16 lanes' values of a tile in the tree order
 // ((g0+g8)+(g4+g12)) + ((g2+g10)+(g6+g14)) for the even lanes and the same
 // over the odd lanes, then even + odd: exchanging with lane ^ 8, ^ 4, ^ 2,
@@ -79,21 +90,21 @@ NV_DEV uint32_t row16_max(uint32_t v) {
 // partners of an exchange hold the same bits) and every lane ends with the
 // tile total.
 NV_DEV float tree16_sum(float e) {
-  e = e + __shfl_xor(e, 8, 64);
-  e = e + __shfl_xor(e, 4, 64);
-  e = e + __shfl_xor(e, 2, 64);
-  e = e + __shfl_xor(e, 1, 64);
+  e = e + bits2f(dpp_x8(f2bits(e)));
+  e = e + bits2f(dpp_x4s(f2bits(e)));
+  e = e + bits2f(dpp_x2(f2bits(e)));
+  e = e + bits2f(dpp_x1(f2bits(e)));
   return e;
 }
 
 // True on every lane of a 16-lane tile iff f holds on all 16 of them.
 NV_DEV bool all16(bool f) {
-  int v = f ? 1 : 0;
-  v &= __shfl_xor(v, 8, 64);
-  v &= __shfl_xor(v, 4, 64);
-  v &= __shfl_xor(v, 2, 64);
-  v &= __shfl_xor(v, 1, 64);
-  return v != 0;
+  uint32_t v = f ? 1u : 0u;
+  v &= dpp_x8(v);
+  v &= dpp_x4s(v);
+  v &= dpp_x2(v);
+  v &= dpp_x1(v);
+  return v != 0u;
 }
 
 NV_DEV uint32_t absmax_bits16(const float v[16]) {

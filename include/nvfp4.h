@@ -57,8 +57,14 @@
  * - e4m3 scale: sigma -> min(sigma, 448) -> round-to-nearest-even, satfinite;
  *   s = decoded scale; encode reciprocal rho = min(1 / (s * S_dec), FLT_MAX).
  * - Element: v = |x'| * rho, rounded to the e2m1 grid (RTN: nearest, ties to
- *   even; SR: up with probability equal to the fractional distance), >= 6
- *   saturates, a NaN v encodes +6 (0x7); sign bit from x'.
+ *   even; SR: up iff u * 2^-16 < f22, u the element's 16-bit draw and f22
+ *   the fractional distance between the two grid points truncated to 22
+ *   bits, so up with probability within 2^-16 of the fractional distance),
+ *   >= 6 saturates, a NaN v encodes +6 (0x7); sign bit from x'.
+ * - Draws: pcg(v) is the "pcg" hash of Jarzynski and Olano ("Hash Functions
+ *   for GPU Rendering"), key = pcg(seed ^ pcg(step ^ 0x9E3779B9)); the pair
+ *   of elements 2p, 2p + 1 (global indices) takes the word w = pcg(p ^ key),
+ *   element 2p the draw w & 0xFFFF and element 2p + 1 the draw w >> 16.
  * - Dequantize: x_hat = (val * s) * S_dec in fp32, then bf16 round-to-nearest-
  *   even (NaN -> 0x7FC0) when the output is bf16.
  */

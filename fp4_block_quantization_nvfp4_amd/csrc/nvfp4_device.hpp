@@ -289,42 +289,18 @@ NV_DEV uint32_t hw_fp4_sr_pair(float a, float b, uint32_t nw) {
   return (ra & 0x0F0F0F0Fu) | (rb & 0xF0F0F0F0u);
 }
 
-// Stochastic conversion of one pair into byte SEL of c, the other bytes of
-// c kept: the instruction writes only the selected byte of its destination
-// register, and the tied operand makes that register c's.
-template <int SEL>
-NV_DEV uint32_t sr_cvt_into(uint32_t c, nv_f2 p, uint32_t seed) {
-  if constexpr (SEL == 0)
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0" : "+v"(c) : "v"(p), "v"(seed));
-  else if constexpr (SEL == 1)
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(c) : "v"(p), "v"(seed));
-  else if constexpr (SEL == 2)
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(c) : "v"(p), "v"(seed));
-  else
-    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(c) : "v"(p), "v"(seed));
-  return c;
-}
-
 // Codes of eight elements x[0..7] * rho (two per byte, even element low)
-// with the complemented draw words nw[0..3] of their four pairs: the four
-// pairs converted into one word with the first-slot seeds (low nibbles) and
-// into another with the second-slot seeds (high nibbles), then merged.
+// with the complemented draw words nw[0..3] of their four pairs.
 NV_DEV uint32_t hw_fp4_sr_word(const float* x, float rho, const uint32_t* nw) {
-  uint32_t ca = any_u32(), cb = any_u32();
-  nv_f2 p;
-  p.x = x[0] * rho; p.y = x[1] * rho;
-  ca = sr_cvt_into<0>(ca, p, (nw[0] << 16) | 0xFFFFu);
-  cb = sr_cvt_into<0>(cb, p, (nw[0] >> 1) | 0x7FFFu);
-  p.x = x[2] * rho; p.y = x[3] * rho;
-  ca = sr_cvt_into<1>(ca, p, (nw[1] << 16) | 0xFFFFu);
-  cb = sr_cvt_into<1>(cb, p, (nw[1] >> 1) | 0x7FFFu);
-  p.x = x[4] * rho; p.y = x[5] * rho;
-  ca = sr_cvt_into<2>(ca, p, (nw[2] << 16) | 0xFFFFu);
-  cb = sr_cvt_into<2>(cb, p, (nw[2] >> 1) | 0x7FFFu);
-  p.x = x[6] * rho; p.y = x[7] * rho;
-  ca = sr_cvt_into<3>(ca, p, (nw[3] << 16) | 0xFFFFu);
-  cb = sr_cvt_into<3>(cb, p, (nw[3] >> 1) | 0x7FFFu);
-  return (ca & 0x0F0F0F0Fu) | (cb & 0xF0F0F0F0u);
+  const uint32_t t0 = hw_fp4_sr_pair<0>(x[0] * rho, x[1] * rho, nw[0]);
+  const uint32_t t1 = hw_fp4_sr_pair<1>(x[2] * rho, x[3] * rho, nw[1]);
+  const uint32_t t2 = hw_fp4_sr_pair<2>(x[4] * rho, x[5] * rho, nw[2]);
+  const uint32_t t3 = hw_fp4_sr_pair<3>(x[6] * rho, x[7] * rho, nw[3]);
+  // byte j of t_j holds pair j; byte permutes gather them (selector byte
+  // 0-3: that byte of the second operand, 4-7: of the first, 0x0C: zero)
+  const uint32_t lo = __builtin_amdgcn_perm(t1, t0, 0x0C0C0500u);  // t0 byte 0, t1 byte 1
+  const uint32_t hi = __builtin_amdgcn_perm(t3, t2, 0x07020C0Cu);  // t2 byte 2, t3 byte 3
+  return lo | hi;
 }
 
 // gfx950 fp32 -> e4m3 of two scales in [0, 448] (bytes 0 and 1): equal to

@@ -168,6 +168,23 @@ def test_quantize_2d(shape, bf16, stochastic, global_scale, tf):
     assert_bitwise(to_np(got), want, "tile dequant")
 
 
+@pytest.mark.parametrize("shape", [(48, 528), (80, 1040), (272, 16), (528, 48), (544, 1552)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("stochastic", [False, True], ids=["rtn", "sr"])
+def test_quantize_2d_strip_groups(shape, stochastic):
+    """Strip counts that leave a lone strip or a partial group at the end of
+    a workgroup (3, 5, 17, 33, 34 strips of 16 rows) and ragged last column
+    groups (a column group covers 512 columns), bf16 with a per-tensor amax."""
+    M, K = shape
+    x = wide_input(M * 7 + K, M, K, True, lo=-6, hi=6)
+    A = oracle.amax(x)
+    wr, wc, ws = oracle.quantize_2d(x, stochastic=stochastic, seed=21, step=3, global_amax=A)
+    r, c, s = nv.quantize_2d(to_dev(x), torch.tensor([A], device="cuda"), stochastic=stochastic, seed=21, step=3)
+    assert_bitwise(to_np(s), ws, "tile scales")
+    assert_bitwise(to_np(r), wr, "rowwise")
+    assert_bitwise(to_np(c), wc, "columnwise")
+
+
 def test_2d_transposition_invariance_on_gpu():
     x = wide_input(99, 64, 128, True, lo=-4, hi=4)
     xt = np.ascontiguousarray(x.T)

@@ -244,7 +244,7 @@ nvfp4_status nvfp4_selftest_launch_plan(int entry, int64_t M, int64_t K, int in_
     case 2: p = nvfp4::plan_4over6(in_bf16 != 0, M, K); break;
     case 3: p = nvfp4::plan_quant2d(M, K); break;
     case 4: p = nvfp4::plan_rowcol(M, K, variant != 0); break;
-    case 5: p = nvfp4::plan_4over6_2d(M, K); break;
+    case 5: p = nvfp4::plan_4over6_2d(M, K, variant != 0); break;
     default: p = nvfp4::plan_amax(M, K, variant != 0); break;
   }
   plan[0] = p.kernel;

@@ -208,7 +208,7 @@ NV_DEV void flush_columns(const uint2* colbuf, const uint8_t* csbuf, int64_t cg,
   for (int cc = threadIdx.x >> 4; cc < NT; cc += NT / 16) {
     const int64_t col = cg * NT + cc;
     if (col < K && q < nst) {
-      const int64_t strip = sg * STR + q;
+      const int64_t strip = sg * STR + q;  // STR strips per workgroup
       *reinterpret_cast<uint2*>(packed_col + col * (M / 2) + strip * 8) = colbuf[cc * (STR + 1) + q];
       if (scales_col) scales_col[col * (M / 16) + strip] = csbuf[cc * (STR + 1) + q];
     }
@@ -321,15 +321,17 @@ __global__ __launch_bounds__(NT) void k_rowcol(
   flush_columns<NT, STR>(colbuf, csbuf, cg, sg, nst, M, K, packed_col, scales_col);
 }
 
+// str: strips per workgroup (STR with columnwise output, at most STR
+// rowwise only; tile_strips_4over6_2d).
 template <typename InT, bool MSE, bool COL, int NT, int STR>
 __global__ __launch_bounds__(NT) void k_4over6_2d(
     const InT* __restrict__ x, const float* __restrict__ global_amax, float D, int64_t M, int64_t K,
     uint8_t* __restrict__ packed_row, uint8_t* __restrict__ packed_col,
-    uint8_t* __restrict__ tile_scales, int64_t ncolg) {
+    uint8_t* __restrict__ tile_scales, int64_t ncolg, int str) {
   __shared__ float rhoT[128];
   __shared__ uint2 colbuf[COL ? NT * (STR + 1) : 1];
   const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
-  const int64_t nwork = ncolg * ((M / 16 + STR - 1) / STR);
+  const int64_t nwork = ncolg * ((M / 16 + str - 1) / str);
   const int64_t w = xcd_work_index(nwork);
   if (w >= nwork) return;  // grid padding (uniform over the workgroup)
   // work items run from the bottom of the tensor up (see xcd_work_index)
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
   const int64_t col0 = cg * NT + 16 * t;
   const bool active = col0 < K;
   const int64_t nstrips = M / 16;
-  const int nst = (int)((nstrips - sg * STR) < STR ? (nstrips - sg * STR) : STR);
+  const int nst = (int)((nstrips - sg * str) < str ? (nstrips - sg * str) : str);
 
   const float A = global_amax[0];
   float S_enc, S_dec;
@@ -347,13 +349,13 @@ __global__ __launch_bounds__(NT) void k_4over6_2d(
   __syncthreads();
 
   // unconditional loads (as in k_rowcol); the body is too large to unroll
-  const InT* lp = x + (sg * STR * 16 + r) * K + (active ? col0 : K - 16);
+  const InT* lp = x + (sg * str * 16 + r) * K + (active ? col0 : K - 16);
   auto load = [&](int st, Raw16<InT>& d) {
     d.load(st < nst ? lp : x);
     lp += 16 * K;
   };
   auto body = [&](int st, const Raw16<InT>& cur) {
-    const int64_t row0 = (sg * STR + st) * 16;
+    const int64_t row0 = (sg * str + st) * 16;
     const int64_t row = row0 + r;
     float v[16];
     uint32_t ab = 0;
@@ -493,10 +495,12 @@ static int launch_4over6_2d_t(const InT* x, const float* ga, float D, int64_t M,
                               uint8_t* pr, uint8_t* pc, uint8_t* ts, hipStream_t st) {
   constexpr int NT = k46TileThreads, STR = k46TileStrips;
   const int64_t ncolg = ceil_div(K, NT);
-  const LaunchPlan pl = plan_4over6_2d(M, K);
+  const int col = pc != nullptr;
+  const int str = tile_strips_4over6_2d(M, K, col);  // STR whenever col
+  const LaunchPlan pl = plan_4over6_2d(M, K, col);
   const dim3 grid((unsigned)pl.grid), block(pl.block);
-  if (pc) hipLaunchKernelGGL((k_4over6_2d<InT, MSE, true, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg);
-  else hipLaunchKernelGGL((k_4over6_2d<InT, MSE, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg);
+  if (col) hipLaunchKernelGGL((k_4over6_2d<InT, MSE, true, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg, str);
+  else hipLaunchKernelGGL((k_4over6_2d<InT, MSE, false, NT, STR>), grid, block, 0, st, x, ga, D, M, K, pr, pc, ts, ncolg, str);
   return (int)hipGetLastError();
 }
 

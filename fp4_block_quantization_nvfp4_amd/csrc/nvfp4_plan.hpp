@@ -84,9 +84,22 @@ inline LaunchPlan plan_rowcol(int64_t M, int64_t K, int four_over_six) {
   return {PLAN_ROWCOL, 1, xcd_grid(ceil_div(K, nt) * ceil_div(M / 16, rowcol_strips(four_over_six))), nt};
 }
 
-inline LaunchPlan plan_4over6_2d(int64_t M, int64_t K) {
-  return {PLAN_4OVER6_2D, 1, xcd_grid(ceil_div(K, k46TileThreads) * ceil_div(M / 16, k46TileStrips)),
-          k46TileThreads};
+// Strips per workgroup of the 16x16 four-over-six kernel.  With columnwise
+// output every workgroup takes k46TileStrips (each column's codes leave as
+// one 128-byte segment).  Rowwise only, a shorter walk is taken when the
+// grid would otherwise not give two workgroups per slot of the chip: the
+// largest of 16, 8 and 4 strips with at least 1024 workgroups, else 4.
+inline int tile_strips_4over6_2d(int64_t M, int64_t K, int columnwise) {
+  if (columnwise) return k46TileStrips;
+  const int64_t ncolg = ceil_div(K, k46TileThreads), nstrips = M / 16;
+  for (int str = k46TileStrips; str > 4; str /= 2)
+    if (ncolg * ceil_div(nstrips, str) >= 1024) return str;
+  return 4;
+}
+
+inline LaunchPlan plan_4over6_2d(int64_t M, int64_t K, int columnwise) {
+  const int str = tile_strips_4over6_2d(M, K, columnwise);
+  return {PLAN_4OVER6_2D, 1, xcd_grid(ceil_div(K, k46TileThreads) * ceil_div(M / 16, str)), k46TileThreads};
 }
 
 inline int64_t amax_partial_groups(int64_t M, int64_t K) {

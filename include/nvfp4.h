@@ -300,7 +300,8 @@ nvfp4_status nvfp4_selftest_scan(int kind, uint32_t param, uint64_t first, uint6
  * shape against the dispatch limits.
  *   entry    0 quantize / qdq, 1 dequantize (variant 1: 16x16 tiles),
  *            2 quantize_4over6, 3 quantize_2d, 4 quantize_rowcol (variant 1:
- *            four-over-six), 5 quantize_4over6_2d, 6 amax (variant 1: per row;
+ *            four-over-six), 5 quantize_4over6_2d (variant 1: with the
+ *            columnwise output), 6 amax (variant 1: per row;
  *            for per tensor the plan is the partial pass).
  *   in_bf16  input dtype (it selects the four-over-six kernel).
  *   plan     HOST pointer to four int64: {kernel id, launches, workgroups of

@@ -124,7 +124,7 @@ def _plan(entry, M, K, bf16=1, variant=0):
 
 
 @pytest.mark.parametrize("entry,variant", [(0, 0), (1, 0), (1, 1), (2, 0), (3, 0), (4, 0), (4, 1), (5, 0),
-                                           (6, 0), (6, 1)])
+                                           (5, 1), (6, 0), (6, 1)])
 @pytest.mark.parametrize("bf16", [0, 1])
 def test_launch_geometry_within_dispatch_limits(entry, variant, bf16):
     """Every accepted shape, down to 16-element rows with the largest M the
@@ -147,6 +147,24 @@ def test_launch_geometry_within_dispatch_limits(entry, variant, bf16):
     assert _plan(2, 8192, 7168, bf16=0)[1][0] == 3           # fp32 takes the generic kernel
     assert _plan(3, 24, 32)[0] == L.E_SHAPE and _plan(7, 16, 16)[0] == L.E_ARG
     assert _plan(0, 1 << 22, 1 << 12)[0] == L.E_RANGE
+
+
+def test_tile_kernel_strips_per_workgroup():
+    """The 16x16 four-over-six kernel walks 16 strips per workgroup with the
+    columnwise output; rowwise only it takes the largest of 16, 8 and 4
+    strips that still gives 1024 workgroups (else 4), so small tensors fill
+    the chip."""
+    def grid(M, K, col):
+        st, (kern, launches, g, block) = _plan(5, M, K, 1, col)
+        assert st == L.OK and kern == 6 and block == 512
+        return g
+    xcd = lambda n: 8 * ((n + 7) // 8)
+    assert grid(7168, 18432, 1) == xcd(36 * 28)       # columnwise: 16 strips
+    assert grid(8192, 7168, 1) == xcd(14 * 32)
+    assert grid(8192, 7168, 0) == xcd(14 * 128)       # rowwise: 4 strips
+    assert grid(8192, 2048, 0) == xcd(4 * 128)
+    assert grid(32768, 2048, 0) == xcd(4 * 256)       # 8 strips reach 1024
+    assert grid(131072, 7168, 0) == xcd(14 * 512)     # 16 strips
 
 
 def test_amax_noalloc_rejects():

@@ -90,6 +90,26 @@ def _mixed_tiles():
     return workloads.bf16_bits(x)
 
 
+@pytest.mark.parametrize("shape", [(8192, 7168), (32768, 2048), (8192, 16384)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_4over6_2d_rowwise_strip_counts(shape):
+    """Rowwise only, the 16x16 kernel walks 4, 8 or 16 strips per workgroup
+    depending on the grid (8192x7168: 4, 32768x2048: 8, 8192x16384: 16); its
+    codes and tile scales equal those of the columnwise launch (16 strips)
+    everywhere, and the oracle's on the first and last strips."""
+    M, K = shape
+    x = wide_input(M + K, M, K, True, lo=-6, hi=6)
+    A = oracle.amax(x)
+    xd = to_dev(x)
+    pr, pc, ts = nv.quantize_4over6_2d(xd, _ga(A), err_mode="mae")
+    pr2, pc2, ts2 = nv.quantize_4over6_2d(xd, _ga(A), err_mode="mae", columnwise=False)
+    assert pc2 is None
+    assert torch.equal(pr, pr2) and torch.equal(ts, ts2)
+    for rows in (slice(0, 16), slice(M - 16, M)):
+        wpr, _, wts = oracle.quantize_4over6_2d(x[rows], A, err_mode="mae")
+        assert_bitwise(to_np(pr2[rows]), wpr, "row codes")
+        assert_bitwise(to_np(ts2[rows.start // 16:rows.stop // 16]), wts, "tile scales")
+
+
 @pytest.mark.parametrize("err", ["mae", "mse"])
 def test_4over6_2d_picks_both_candidates(err):
     x = _mixed_tiles()

@@ -1,7 +1,8 @@
 """Benchmark: NVFP4 four-over-six quantize throughput on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--err mae|mse]
-                    [--no-cpu] [--no-extra] [--only WORKLOAD] [--copy-calib]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-ms T]
+                    [--err mae|mse] [--no-cpu] [--no-extra] [--only WORKLOAD]
+                    [--copy-calib]
 
 Workload (the metric's configuration): row-scaled four-over-six NVFP4
 quantize of an 8192x7168 bf16 activation (N(0,1) with a log-uniform per-row
@@ -23,6 +24,8 @@ traffic from the committed rocprofv3 counter summary while it matches the
 current kernel source) and the CPU oracle timed over a process pool of every
 core this process may use.  Unless --no-extra, the other workloads are timed
 too (each parity-checked on a sample first) and reported under "extra".
+Every timed region follows an untimed warmup of at least W steps (W/4 for
+the extras) and at least --warmup-ms (30) of GPU time.
 `--only NAME` runs one workload's steps alone (for rocprofv3 runs).
 """
 from __future__ import annotations
@@ -127,6 +130,34 @@ def time_ms(torch, fn, warmup, steps, host=None):
     if host is not None:
         host["us_per_call"] = (h1 - h0) * 1e6 / steps
     return t0.elapsed_time(t1) / steps
+
+
+def warm(torch, fn, min_steps, min_ms, cap=4000):
+    """Untimed warmup: at least `min_steps` steps and at least `min_ms` of GPU
+    time (batches of 8 steps timed by events; exactly `min_steps` when
+    `min_ms` is 0), at most `cap` steps.  Back-to-back launches that follow
+    an idle GPU (the parity check runs on the CPU) run well below their
+    steady rate for several milliseconds (the four-over-six row kernel: 33
+    -> 42 -> 35 us per launch over its first ~7 ms); a fixed handful of
+    warmup steps would fold that transient into the timed region.  Returns
+    the steps run."""
+    if min_ms <= 0:
+        for i in range(min_steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return min_steps
+    n, t = 0, 0.0
+    while (n < min_steps or t < min_ms) and n < cap:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(8):
+            fn(n + k)
+        e1.record()
+        torch.cuda.synchronize()
+        t += e0.elapsed_time(e1)
+        n += 8
+    return n
 
 
 def copy_ceiling_gbs(torch, nbytes=1 << 30, reps=10):
@@ -469,6 +500,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-ms", type=float, default=30.0,
+                    help="untimed warmup also lasts at least this much GPU time (0: exactly --warmup steps)")
     ap.add_argument("--err", choices=["mae", "mse"], default="mae")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="time only the metric workload")
@@ -523,13 +556,17 @@ def main():
     m = build_metric(c, args.err)
     m["check"]()  # parity before timing (sampled rows; rows are independent on this path)
     host = {}
-    ms = time_ms(torch, m["step"], args.warmup, args.steps, host)
+    # untimed: at least W steps and at least --warmup-ms of GPU time, so the
+    # timed region starts in the steady state (see warm())
+    nwarm = warm(torch, m["step"], args.warmup, args.warmup_ms)
+    ms = time_ms(torch, m["step"], 0, args.steps, host)
     algo = m["bytes"]
     gbs = algo / (ms * 1e-3) / 1e9
     metric_name = f"act_rows_8192x7168_4over6_{args.err}"
     rl = roofline(algo, ms, metric_name, "k_4over6_rows (row amax computed in-pass)")
     rl.update({"timing": "HIP events on the launch stream around the timed region; one launch of the kernel "
-                         "per step, so region time / steps bounds its average duration from above",
+                         "per step, so region time / steps bounds its average duration from above; untimed "
+                         f"warmup of at least {args.warmup} steps and {args.warmup_ms:g} ms of GPU time first",
                "host_submit_us_per_launch": round(host["us_per_call"], 3),
                "copy_ceiling_GBs": round(copy_ceiling_gbs(torch), 1)})
     line = {
@@ -539,6 +576,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": nwarm,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -565,10 +603,12 @@ def main():
                 continue
             b = build()
             b["check"]()
-            ms_b = time_ms(torch, b["step"], warmup, steps)
+            nw = warm(torch, b["step"], warmup, args.warmup_ms)
+            ms_b = time_ms(torch, b["step"], 0, steps)
             r = roofline(b["bytes"], ms_b, name, b["kernel"])
             extra[name] = {"us": r["avg_launch_us"], "GB/s": r["achieved"], "frac_hbm": r["frac"],
-                           "bytes": b["bytes"], "traffic": r["traffic"], "note": b["note"]}
+                           "bytes": b["bytes"], "traffic": r["traffic"], "steps": steps, "warmup": nw,
+                           "note": b["note"]}
             del b
         line["extra"] = extra
 

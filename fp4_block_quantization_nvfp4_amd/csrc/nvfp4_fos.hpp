@@ -91,12 +91,28 @@ NV_DEV float candidate(const float xv[16], float s, float rho, float A, float D,
 //   |Z_c - T| <= 4.02 u S + 19.1 u T            (1x16; 23.1 u T for tiles).
 // Hence |Z_c - E_c| <= 6.04 u S + 37.2 u T (45.2 u T), and with S <= 16 a
 // (256 a) both candidates together stay below 194 u a + 38 u (Z_4 + Z_6)
-// (3092 u a + 46 u (Z_4 + Z_6) for tiles).  For MSE (E'_c = sum (v_i - q_i)^2,
-// Z_c = W_c^2 E'_c) the same steps with |x_i| |t_i| <= (x_i^2 + t_i^2) / 2
-// give 193 u a^2 + 51 u (Z_4 + Z_6) (3084 u a^2 + 59 u (...) for tiles).  The
-// margin B = k a (or k a^2) + 2^-15 (Z_4 + Z_6) + 2^-90, k = 2^-15 for 1x16
-// and 2^-11 for tiles, covers these at least 2.6 times over (the 2^-90 term
-// covers subnormal products), so
+// (3092 u a + 46 u (Z_4 + Z_6) for tiles).  The margin B = k a + 2^-15 (Z_4
+// + Z_6) + 2^-90, k = 2^-15 for 1x16 and 2^-11 for tiles, covers these at
+// least 2.6 times over (the 2^-90 term covers subnormal products).
+// For MSE (E'_c = sum (v_i - q_i)^2, Z_c = W_c^2 E'_c) let T_i = |x_i| - q_i c
+// and E* = sum T_i^2.  Here v_i - q_i is exact (Sterbenz: v_i <= 12 in the
+// guards), W_c (v_i - q_i) = (1 + g) T_i + |x_i| xi_i with |g| <= 2.01 u,
+// |xi_i| <= 4.02 u, and |x_i - d_i| = T_i - q_i c beta_i, |beta_i| <= 2.01 u,
+// so both sides carry cross terms sum |T_i| |x_i| <= 4 a sqrt(E*)
+// (Cauchy-Schwarz over 16 elements of magnitude <= a):
+//   |E_c - E*| <= 22.2 u E* + 16.2 u a sqrt(E*) + 132 u^2 a^2,
+//   |Z_c - E*| <= 22.1 u E* + 32.3 u a sqrt(E*) + 260 u^2 a^2.
+// The second gives sqrt(E*) <= (1 + 22.2 u) sqrt(Z_c) + 48.6 u a, hence
+// |Z_c - E_c| <= 44.4 u Z_c + 48.6 u a sqrt(Z_c) + 2750 u^2 a^2, and for both
+// candidates (sqrt(Z_4) + sqrt(Z_6) <= sqrt(2 (Z_4 + Z_6))) at most
+// 44.4 u (Z_4 + Z_6) + 68.8 u a sqrt(Z_4 + Z_6) + 5500 u^2 a^2.  A 1x16 MSE
+// margin B = 2^-16 a sqrt(Z_4 + Z_6) + 2^-30 a^2 + 2^-15 (Z_4 + Z_6) + 2^-90
+// covers these 3.7, 48 and 11.5 times over (the square root is the hardware
+// one, within an ulp; a scale code rounds sigma up by at most 2x, so
+// W_c <= (a / 2)(1 + 6 u) and the a^2 term also covers the absolute error of
+// a subnormal v_i).  Tiles keep the coarser bound with
+// |x_i| |t_i| <= (x_i^2 + t_i^2) / 2: 3084 u a^2 + 59 u (Z_4 + Z_6), margin
+// 2^-11 a^2 + 2^-15 (Z_4 + Z_6) + 2^-90.  Then
 //   Z_4 + B < Z_6  proves E_4 < E_6 (map-to-4), and
 //   Z_4 - B >= Z_6 proves E_4 >= E_6 (map-to-6, ties included).
 // The range guards (2^-50 <= W_6 <= W_4 <= 2^50, a <= 2^50, finite Z, no
@@ -199,6 +215,14 @@ NV_DEV bool same_dequant16(const uint32_t c6[2], const uint32_t c4[2], float s6,
 // guards (use exact_error16), -2: outside them (use the software
 // candidate).  kLog2N = 4 for a 1x16 block, 8 for a 16x16 tile (E6a / E4a
 // then the tile totals).
+// The 1x16 MSE margin of the comment above: 2^-16 a sqrt(Zs) + 2^-30 a^2 +
+// 2^-15 Zs + 2^-90 with Zs = Z4 + Z6 (finite and at most 2^111 inside the
+// range guards).
+NV_DEV float mse_margin16(float a, float Zs) {
+  return __builtin_fmaf(a, __builtin_fmaf(__builtin_amdgcn_sqrtf(Zs), 0x1p-16f, a * 0x1p-30f),
+                        __builtin_fmaf(Zs, 0x1p-15f, 0x1p-90f));
+}
+
 template <bool MSE, int kLog2N>
 NV_DEV int certified_pick(float E6a, float E4a, float W6, float W4, float a) {
   if (!(W6 >= 0x1p-50f && W4 <= 0x1p50f && a <= 0x1p50f)) return -2;
@@ -207,7 +231,8 @@ NV_DEV int certified_pick(float E6a, float E4a, float W6, float W4, float a) {
   const float Z4 = MSE ? (W4 * W4) * E4a : W4 * E4a;
   if (!(Z6 <= kFltMax && Z4 <= kFltMax)) return -2;
   constexpr float kA = kLog2N == 4 ? 0x1p-15f : 0x1p-11f;
-  const float B = kA * (MSE ? a * a : a) + 0x1p-15f * (Z4 + Z6) + 0x1p-90f;
+  const float B = (MSE && kLog2N == 4) ? mse_margin16(a, Z4 + Z6)
+                                       : kA * (MSE ? a * a : a) + 0x1p-15f * (Z4 + Z6) + 0x1p-90f;
   if (Z4 + B < Z6) return 1;
   if (Z4 - B >= Z6) return 0;
   return -1;
@@ -312,11 +337,11 @@ NV_DEV bool fos_row_in_range(float A, float S_dec) {
 }
 
 // With WTAB, WT holds W = s * S_dec for every scale code (the same product
-// the block would form), tabulated per row beside rhoT.  The margin is
-// formed as fma(a + (Z4 + Z6), 2^-15, 2^-90) (a^2 for MSE), and the test
-// compares fl(Z6 - Z4) with +-B: the same bound as in certified_pick up to
-// a few roundings of relative size 2^-24, far inside its 2.6x safety factor
-// (fl(Z6 - Z4) > B implies Z6 - Z4 > B / (1 + 2^-24)).
+// the block would form), tabulated per row beside rhoT.  The MAE margin is
+// formed as fma(a + (Z4 + Z6), 2^-15, 2^-90), the MSE one by mse_margin16,
+// and the test compares fl(Z6 - Z4) with +-B: the same bounds as in
+// certified_pick up to a few roundings of relative size 2^-24, far inside
+// their safety factors (fl(Z6 - Z4) > B implies Z6 - Z4 > B / (1 + 2^-24)).
 template <bool MSE, bool TIES, bool WTAB = false>
 NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S_enc, float S_dec,
                                 float A, float D, const float* rhoT, uint32_t c[2],
@@ -332,7 +357,7 @@ NV_DEV uint32_t fos_block_plain(const float xv[16], float a, bool plain, float S
   const float W4 = WTAB ? WT[k4] : hw_e4m3_value<1>(kk) * S_dec;
   const float Z6 = (MSE ? W6 * W6 : W6) * E6a;
   const float Z4 = (MSE ? W4 * W4 : W4) * E4a;
-  const float B = __builtin_fmaf((MSE ? a * a : a) + (Z4 + Z6), 0x1p-15f, 0x1p-90f);
+  const float B = MSE ? mse_margin16(a, Z4 + Z6) : __builtin_fmaf(a + (Z4 + Z6), 0x1p-15f, 0x1p-90f);
   const float dZ = Z6 - Z4;
   int pick;
   if (dZ > B) {

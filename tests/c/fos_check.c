@@ -15,12 +15,16 @@
  *   order (MSE: E' = fma(t, t, E')), W_c = s_c S_dec, Z_c = W_c E'_c
  *   (MSE: (W_c W_c) E'_c; tiles tree-sum E' first).
  *   - the lean test of plain 1x16 blocks: B = fma(a + (Z4 + Z6), 2^-15,
- *     2^-90) (a^2 for MSE), dZ = Z6 - Z4: map-to-4 iff dZ > B, map-to-6 iff
- *     dZ <= -B, else undecided;
+ *     2^-90) for MAE, the 1x16 MSE margin below for MSE, dZ = Z6 - Z4:
+ *     map-to-4 iff dZ > B, map-to-6 iff dZ <= -B, else undecided;
  *   - the guarded test (blocks outside the plain class, and 16x16 tiles):
  *     B = k a + 2^-15 (Z4 + Z6) + 2^-90 (k = 2^-15 for 1x16, 2^-11 for
- *     tiles; a^2 for MSE): map-to-4 iff Z4 + B < Z6, map-to-6 iff
- *     Z4 - B >= Z6, else undecided; range guards as in the kernel.
+ *     tiles; for MSE tiles k a^2, for MSE 1x16 blocks the 1x16 MSE margin):
+ *     map-to-4 iff Z4 + B < Z6, map-to-6 iff Z4 - B >= Z6, else undecided;
+ *     range guards as in the kernel.
+ *   - the 1x16 MSE margin: fma(a, fma(sqrt(Zs), 2^-16, a 2^-30),
+ *     fma(Zs, 2^-15, 2^-90)) with Zs = Z4 + Z6 (correctly rounded sqrtf
+ *     here; the kernels' hardware square root is within an ulp of it).
  *   - undecided blocks: the kernel's exact sums, d_i = 2^k fl(fl(mu s A) / D)
  *     for q_i = mu 2^k (mu in {1, 1.5}), and the identical-dequant test.
  *
@@ -140,10 +144,14 @@ static float tree16(const float* g) {
 }
 
 /* kernel decisions: 1 map-to-4, 0 map-to-6, -1 undecided, -2 outside guards */
+static float mse_margin16(float a, float Zs) {
+  return fmaf(a, fmaf(sqrtf(Zs), 0x1p-16f, a * 0x1p-30f), fmaf(Zs, 0x1p-15f, 0x1p-90f));
+}
+
 static int lean_pick(int mse, float E6a, float E4a, float W6, float W4, float a, double* ratio_den) {
   const float Z6 = (mse ? W6 * W6 : W6) * E6a;
   const float Z4 = (mse ? W4 * W4 : W4) * E4a;
-  const float B = fmaf((mse ? a * a : a) + (Z4 + Z6), 0x1p-15f, 0x1p-90f);
+  const float B = mse ? mse_margin16(a, Z4 + Z6) : fmaf(a + (Z4 + Z6), 0x1p-15f, 0x1p-90f);
   const float dZ = Z6 - Z4;
   *ratio_den = B;
   if (dZ > B) return 1;
@@ -160,7 +168,8 @@ static int guarded_pick(int mse, int log2n, float E6a, float E4a, float W6, floa
   const float Z4 = mse ? (W4 * W4) * E4a : W4 * E4a;
   if (!(Z6 <= kFltMax && Z4 <= kFltMax)) return -2;
   const float kA = log2n == 4 ? 0x1p-15f : 0x1p-11f;
-  const float B = kA * (mse ? a * a : a) + 0x1p-15f * (Z4 + Z6) + 0x1p-90f;
+  const float B = (mse && log2n == 4) ? mse_margin16(a, Z4 + Z6)
+                                      : kA * (mse ? a * a : a) + 0x1p-15f * (Z4 + Z6) + 0x1p-90f;
   *ratio_den = B;
   if (Z4 + B < Z6) return 1;
   if (Z4 - B >= Z6) return 0;

@@ -195,13 +195,14 @@ def test_weight_2d_four_over_six_tiles_every_strip(err):
     assert_bitwise(to_np(pc), wc, "columnwise codes (every strip)")
 
 
-@pytest.mark.parametrize("fos", [False, True], ids=["standard", "four_over_six"])
-def test_weight_2d_rowcol_every_block(fos):
+@pytest.mark.parametrize("fos,err", [(False, "mae"), (True, "mae"), (True, "mse")],
+                         ids=["standard", "four_over_six", "four_over_six_mse"])
+def test_weight_2d_rowcol_every_block(fos, err):
     x, xd, A, Af = _weight_2d()
     M, K = x.shape
-    got = [to_np(t) for t in nv.quantize_rowcol(xd, A, four_over_six=fos)]
+    got = [to_np(t) for t in nv.quantize_rowcol(xd, A, four_over_six=fos, err_mode=err)]
     bound = 256.0 if fos else 448.0
-    res = P.starmap(T.rowcol, [(x[a:b], Af, fos, "mae", bound) for a, b in P.row_chunks(M, 16)])
+    res = P.starmap(T.rowcol, [(x[a:b], Af, fos, err, bound) for a, b in P.row_chunks(M, 16)])
     want = P.concat(res, axis=(0, 0, 1, 1))
     for g, w, what in zip(got, want, ("row codes", "row scales", "col codes", "col scales")):
         assert_bitwise(g, w, f"{what} (every block)")

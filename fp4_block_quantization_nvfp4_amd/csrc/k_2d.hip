@@ -180,7 +180,9 @@ __global__ __launch_bounds__(k2dThreads) void k_quant2d(
     float sigma = GLOBAL ? a * mul : div_guarded(a, 6.0f, 1.0f / 6.0f);
     sigma = fminf(sigma, kE4m3Max);
     uint32_t sc = hw_e4m3_pair(sigma, 0.0f) & 0xFFu;
-    if (UP && e4m3_decode(sc) < sigma && sc < 0x7Eu) sc += 1u;  // truncation-free: smallest e4m3 value >= sigma
+    // truncation-free: smallest e4m3 value >= sigma (sc <= 0x7E here, where
+    // the hardware decode equals e4m3_decode)
+    if (UP && hw_e4m3_value<0>(sc) < sigma && sc < 0x7Eu) sc += 1u;
     const float rho = rhoT[sc];
     float xa[8], xb[8];
     widen8(cur, static_cast<const InT*>(nullptr), xa);

@@ -1,8 +1,8 @@
 """Benchmark: NVFP4 four-over-six quantize throughput on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-ms T]
-                    [--err mae|mse] [--no-cpu] [--no-extra] [--only WORKLOAD]
-                    [--copy-calib]
+                    [--err mae|mse] [--no-cpu] [--no-extra] [--no-pages]
+                    [--only WORKLOAD] [--copy-calib]
 
 Workload (the metric's configuration): row-scaled four-over-six NVFP4
 quantize of an 8192x7168 bf16 activation (N(0,1) with a log-uniform per-row
@@ -467,6 +467,96 @@ def build_heavy(c):
                 note="bf16 in, fp32 residual in/out, bf16 out")
 
 
+# The four-over-six pull request's Bench table (bf16 input, MAE, bound 256,
+# bytes in + out): shape -> CuTe DSL kernel microseconds on GB200 for the
+# 1x16 per-tensor, 1x16 row-scaled and 16x16 rows (other hardware: context).
+PAGES_BENCH_GB200_US = {
+    (8192, 2048): (127.0, 127.0, 131.1),
+    (8192, 7168): (409.6, 413.7, 423.9),
+    (32768, 2048): (464.9, 470.0, 481.3),
+    (32768, 7168): (1572.2, 1592.3, 1631.2),
+    (131072, 2048): (1793.1, 1815.6, 1860.6),
+    (131072, 7168): (6222.9, 6300.8, 6460.5),
+}
+
+
+def pages_bench(c, warmup, steps, warmup_ms):
+    """The pages' benchmark shapes on this GPU: four-over-six MAE, bound 256,
+    bf16 rows N(0,1) with a log-uniform row std in [1e-2, 1e2] drawn on the
+    device (seeded).  Per shape: 1x16 with the per-tensor amax given, 1x16
+    row-scaled with the row amax computed in the pass, and 16x16 per tensor
+    (rowwise output, as the table).  Each variant is checked bit for bit
+    against the oracle on sampled rows (whole 16-row strips for 16x16), then
+    timed like the extras; buffer sets rotate until the footprint passes
+    600 MB."""
+    np, torch, L = c.np, c.torch, c.L
+    out = {}
+    for si, ((M, K), gb200) in enumerate(PAGES_BENCH_GB200_US.items()):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(1000 + si)
+        std = torch.pow(10.0, 4.0 * torch.rand(M, 1, generator=g, device="cuda") - 2.0)
+        x0 = (torch.randn(M, K, generator=g, device="cuda") * std).to(torch.bfloat16)
+        del std
+        nb = M * K * 2 + M * K // 2 + M * K // 16
+        nsets = max(1, min(16, -(-600_000_000 // nb)))
+        xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+        pk = [torch.empty((M, K // 2), dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+        sc = [torch.empty((M, K // 16), dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+        ts = torch.empty((M // 16, K // 16), dtype=torch.uint8, device="cuda")
+        ra = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in range(nsets)]
+        ga = torch.empty(1, dtype=torch.float32, device="cuda")
+        wsz = c.lib.nvfp4_amax_workspace_bytes(M, K)
+        ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device="cuda")
+        _call(c, "nvfp4_amax", c.lib.nvfp4_amax(x0.data_ptr(), L.BF16, M, K, None, L.SCALE_TENSOR, ga.data_ptr(),
+                                                 ws.data_ptr(), wsz, c.stream))
+        A = np.float32(ga.cpu().numpy()[0])
+        assert A == np.float32(x0.abs().max().float().item()), "per-tensor amax"
+        rows = np.unique(np.concatenate([np.arange(16), np.arange(M - 16, M), [M // 2]]))
+        strips = np.concatenate([np.arange(16), np.arange(M - 16, M)])
+        host = lambda r: x0[torch.from_numpy(r).cuda()].cpu().view(torch.int16).numpy().view(np.uint16)
+        xr, xt = host(rows), host(strips)
+        res = {}
+        for vi, name in enumerate(("1x16", "1x16_row_scaled", "16x16")):
+            if name == "16x16":
+                def step(i):
+                    j = i % nsets
+                    _call(c, "nvfp4_quantize_4over6_2d", c.lib.nvfp4_quantize_4over6_2d(
+                        xs[j].data_ptr(), L.BF16, M, K, ga.data_ptr(), L.MAE, 256.0, pk[j].data_ptr(), None,
+                        ts.data_ptr(), c.stream))
+                step(0)
+                torch.cuda.synchronize()
+                wp, wt = c.oracle.quantize_4over6(xt, A, err_mode="mae", bound=256.0, block="16x16")
+                check_rows(np, pk[0].cpu().numpy()[strips], wp, f"pages {M}x{K} 16x16 codes")
+                check_rows(np, ts.cpu().numpy()[[0, M // 16 - 1]], wt, f"pages {M}x{K} 16x16 tile scales")
+                nbytes = M * K * 2 + M * K // 2 + M * K // 256
+            else:
+                row = name != "1x16"
+                def step(i, row=row):
+                    j = i % nsets
+                    a = ra[j].data_ptr() if row else ga.data_ptr()
+                    _call(c, "nvfp4_quantize_4over6", c.lib.nvfp4_quantize_4over6(
+                        xs[j].data_ptr(), L.BF16, M, K, a, L.SCALE_ROW if row else L.SCALE_TENSOR, 0 if row else 1, L.MAE,
+                        256.0, pk[j].data_ptr(), sc[j].data_ptr(), c.stream))
+                step(0)
+                torch.cuda.synchronize()
+                Ar = c.oracle.amax(xr, mode="row") if row else A
+                wp, wsc = c.oracle.quantize_4over6(xr, Ar, err_mode="mae", bound=256.0)
+                if row:
+                    check_rows(np, ra[0].cpu().numpy()[rows], Ar, f"pages {M}x{K} row amax")
+                check_rows(np, pk[0].cpu().numpy()[rows], wp, f"pages {M}x{K} {name} codes")
+                check_rows(np, sc[0].cpu().numpy()[rows], wsc, f"pages {M}x{K} {name} scales")
+                nbytes = nb
+            warm(torch, step, warmup, warmup_ms)
+            ms = time_ms(torch, step, 0, steps)
+            res[name] = {"us": round(ms * 1e3, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 2),
+                         "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "gb200_us": gb200[vi]}
+        out[f"{M}x{K}"] = res
+        del xs, pk, sc, ts, ra, x0, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def builders(c, W):
     """Workload name -> builder (the extra workloads and the metric's MSE form)."""
     w2 = lambda kind: (lambda: build_2d(c, W(), kind))
@@ -505,6 +595,7 @@ def main():
     ap.add_argument("--err", choices=["mae", "mse"], default="mae")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="time only the metric workload")
+    ap.add_argument("--no-pages", action="store_true", help="skip the pages' benchmark shapes")
     ap.add_argument("--only", default=None, help="run only this workload's steps (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calib", action="store_true",
@@ -611,6 +702,14 @@ def main():
                            "note": b["note"]}
             del b
         line["extra"] = extra
+
+    if not args.no_pages:
+        line["pages_bench"] = {
+            "note": "the four-over-six pull request's Bench shapes: bf16 rows N(0,1) x log-uniform row std "
+                    "[1e-2,1e2] (seeded, drawn on the device), MAE, bound 256, checked bit for bit on sampled "
+                    "rows first; GB/s = bytes in + out as there; 16x16 rowwise output; gb200_us = the pages' "
+                    "CuTe DSL kernel on GB200 (other hardware, context only)",
+            "shapes": pages_bench(c, max(args.warmup // 4, 3), max(args.steps // 4, 10), args.warmup_ms)}
 
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(np, m["x_bits"], args.err, args.cpu_seconds)

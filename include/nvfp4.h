@@ -18,7 +18,8 @@
  *   the pair index i >> 1 of the random-number generator fits 32 bits.
  * - All pointers are DEVICE pointers, owned by the caller, allocated on the
  *   device that is current when the call is made.  The library allocates no
- *   memory and keeps no state; calls are asynchronous on `stream` (a
+ *   memory and keeps no state other than the fixed scratch array of
+ *   nvfp4_amax_noalloc; calls are asynchronous on `stream` (a
  *   hipStream_t; NULL is the default stream) and return once the kernels are
  *   queued.  Outputs must not overlap inputs, except that nvfp4_qdq may
  *   write `out` over `x` when both have the same dtype.

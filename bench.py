@@ -602,9 +602,9 @@ def main():
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by rows with no exchange except a 4-byte amax max-reduce; "
-              "see the sharding note in the design document).", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard by rows, its only exchange a 4-byte max all-reduce of the "
+              "per-tensor amax, with the generator keyed by global element indices).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
